@@ -1,0 +1,461 @@
+"""Pins for the CPU oracle: checks against what mathematics fixes, independent of
+the oracle's own formulas (brute force, closed forms, invariants, library routines
+on special cases, hand-worked fixtures). CPU only."""
+import json
+import math
+import os
+from itertools import product
+
+import numpy as np
+import pytest
+
+from oracle import flashcache_oracle as O
+from kv_cache_attention_step_amd import workload as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_ties_and_fixed_points():
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to the even mantissa (1.0)
+    assert O.round_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    # 1 + 3*2^-8 is halfway between 1+2^-7 (odd) and 1+2^-6 (even)
+    assert O.round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+    assert O.round_bf16(np.array([-(1 + 2.0 ** -8 + 2.0 ** -20)]))[0] == -(1 + 2.0 ** -7)
+    # every finite bf16 value is a fixed point
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = O.bf16_to_f64(bits)
+    fin = np.isfinite(vals) & (vals != 0) & (np.abs(vals) >= 2.0 ** -126)
+    np.testing.assert_array_equal(O.round_bf16(vals[fin]), vals[fin])
+
+
+def test_round_bf16_matches_integer_rounding_of_float32_bits():
+    # an independent implementation: integer round-half-even on the float32 bits
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    ours = O.round_bf16(x.astype(np.float64))
+    ref = W.bf16_bits_to_f32(W.to_bf16_bits(x)).astype(np.float64)
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(O.f64_to_bf16_bits(ours), W.to_bf16_bits(x))
+
+
+# ---------------------------------------------------------------------------
+# projection
+# ---------------------------------------------------------------------------
+
+def _tiny_cache(num_pages, H, ps, D, rng, dtype="f32"):
+    kc = rng.standard_normal((num_pages, H, ps, D)).astype(np.float32)
+    vc = rng.standard_normal((num_pages, H, ps, D)).astype(np.float32)
+    return kc, vc
+
+
+def test_projection_matches_brute_force_triple_loop():
+    rng = np.random.default_rng(1)
+    T, H, D = 5, 2, 4
+    d = H * D
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    w = rng.standard_normal((3 * d, d)).astype(np.float32)
+    pos = np.zeros(T, np.int32)          # RoPE at position 0 is the identity
+    table = np.array([[0, 1]], np.int32)
+    kc, vc = _tiny_cache(2, H, 4, D, rng)
+    pos = np.array([0, 0, 0, 0, 0], np.int32)
+    r = O.qkv_rope_cache_write(x, pos, np.array([0, T], np.int32), w, H, D, 1e4, kc, vc, table, 4,
+                               "f32", write_cache=False)
+    y = np.zeros((T, 3 * d))
+    for t in range(T):
+        for n in range(3 * d):
+            acc = 0.0
+            for c in range(d):
+                acc += float(x[t, c]) * float(w[n, c])
+            y[t, n] = acc
+    np.testing.assert_allclose(r["q"].reshape(T, d), y[:, :d], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["k"].reshape(T, d), y[:, d:2 * d], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["v"].reshape(T, d), y[:, 2 * d:], rtol=1e-12, atol=1e-12)
+
+
+def test_projection_identity_weights_give_q_k_v_equal_hidden():
+    rng = np.random.default_rng(2)
+    T, H, D = 3, 2, 4
+    d = H * D
+    x = W.to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    eye = np.eye(d, dtype=np.float32)
+    w = W.to_bf16_bits(np.concatenate([eye, eye, eye], axis=0))
+    kc = W.to_bf16_bits(np.zeros((1, H, 4, D), np.float32))
+    r = O.qkv_rope_cache_write(x, np.zeros(T, np.int32), np.array([0, T], np.int32), w, H, D, 1e4,
+                               kc, kc, np.array([[0]], np.int32), 4, "bf16", write_cache=False)
+    xf = O.bf16_to_f64(x).reshape(T, H, D)
+    for name in ("q", "k", "v"):
+        np.testing.assert_array_equal(r[name], xf)
+
+
+# ---------------------------------------------------------------------------
+# RoPE (rotate-half reading; the variant itself is not fixed by the pages)
+# ---------------------------------------------------------------------------
+
+def test_rope_preserves_pair_norms_and_is_identity_at_zero():
+    rng = np.random.default_rng(3)
+    D = 128
+    x = rng.standard_normal((7, D))
+    pos = np.array([0, 1, 5, 100, 767, 1535, 4095])
+    y = O.rope(x, pos, 500000.0)
+    half = D // 2
+    n_in = np.hypot(x[:, :half], x[:, half:])
+    n_out = np.hypot(y[:, :half], y[:, half:])
+    np.testing.assert_allclose(n_out, n_in, rtol=1e-12)
+    np.testing.assert_array_equal(y[0], x[0])
+
+
+def test_rope_relative_position_property():
+    rng = np.random.default_rng(4)
+    D = 64
+    q = rng.standard_normal((1, D))
+    k = rng.standard_normal((1, D))
+    for m, n, t in [(3, 10, 7), (100, 2, 900), (0, 0, 33)]:
+        a = float((O.rope(q, [m], 1e4) @ O.rope(k, [n], 1e4).T)[0, 0])
+        b = float((O.rope(q, [m + t], 1e4) @ O.rope(k, [n + t], 1e4).T)[0, 0])
+        assert abs(a - b) < 1e-10 * (1 + abs(a))
+
+
+def test_rope_composes_and_turns_each_pair_by_its_frequency():
+    D, base = 8, 10000.0
+    half = D // 2
+    # unit vector in pair e at position 1 turns counter-clockwise by base^(-2e/D)
+    for e in range(half):
+        x = np.zeros((1, D))
+        x[0, e] = 1.0
+        y = O.rope(x, [1], base)[0]
+        ang = math.atan2(y[e + half], y[e])
+        assert abs(ang - base ** (-2.0 * e / D)) < 1e-15
+        # all other coordinates stay zero
+        others = [i for i in range(D) if i not in (e, e + half)]
+        assert np.all(y[others] == 0)
+    # position p then p' equals p + p'
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((1, D))
+    np.testing.assert_allclose(O.rope(O.rope(x, [13], base), [29], base), O.rope(x, [42], base),
+                               rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# paged cache write
+# ---------------------------------------------------------------------------
+
+def test_cache_write_slots_readback_and_untouched_bits():
+    rng = np.random.default_rng(6)
+    H, D, ps = 2, 4, 4
+    table = np.array([[5, 2, 7, -1], [0, 3, 6, 1]], np.int32)   # two sequences
+    num_pages = 8
+    kc = W.to_bf16_bits(rng.standard_normal((num_pages, H, ps, D)).astype(np.float32))
+    vc = W.to_bf16_bits(rng.standard_normal((num_pages, H, ps, D)).astype(np.float32))
+    pos = np.array([1, 6, 9, 0, 4, 15], np.int32)
+    cu = np.array([0, 3, 6], np.int32)
+    d = H * D
+    x = W.to_bf16_bits(rng.standard_normal((6, d)).astype(np.float32))
+    w = W.to_bf16_bits(rng.standard_normal((3 * d, d)).astype(np.float32))
+    r = O.qkv_rope_cache_write(x, pos, cu, w, H, D, 1e4, kc, vc, table, ps, "bf16")
+    # closed-form slots: page = table[b][p // 4], slot = page * 4 + p % 4
+    expect = [5 * 4 + 1, 2 * 4 + 2, 7 * 4 + 1, 0 * 4 + 0, 3 * 4 + 0, 1 * 4 + 3]
+    np.testing.assert_array_equal(r["slot_mapping"], expect)
+    # gather the written rows back through the page table
+    seq = [0, 0, 0, 1, 1, 1]
+    for t in range(6):
+        Kb = O.gather_kv(r["k_cache"], table, seq[t], int(pos[t]) + 1, ps)
+        Vb = O.gather_kv(r["v_cache"], table, seq[t], int(pos[t]) + 1, ps)
+        np.testing.assert_array_equal(Kb[pos[t]], O.round_bf16(r["k"][t]))
+        np.testing.assert_array_equal(Vb[pos[t]], O.round_bf16(r["v"][t]))
+    # every other slot keeps its bits
+    touched = np.zeros((num_pages, ps), bool)
+    for s in expect:
+        touched[s // ps, s % ps] = True
+    old_k = O.bf16_to_f64(kc)
+    old_v = O.bf16_to_f64(vc)
+    for p in range(num_pages):
+        for o in range(ps):
+            if not touched[p, o]:
+                np.testing.assert_array_equal(r["k_cache"][p, :, o], old_k[p, :, o])
+                np.testing.assert_array_equal(r["v_cache"][p, :, o], old_v[p, :, o])
+
+
+# ---------------------------------------------------------------------------
+# attention and importance
+# ---------------------------------------------------------------------------
+
+def _naive_attention(q, k, v, scale):
+    """Explicit loops, written separately from the oracle."""
+    Q, D = q.shape
+    L = k.shape[0]
+    out = np.zeros((Q, v.shape[1]))
+    prob = np.zeros((Q, L))
+    for i in range(Q):
+        s = [sum(q[i, c] * k[j, c] for c in range(D)) * scale for j in range(L)]
+        mx = max(s)
+        e = [math.exp(x - mx) for x in s]
+        tot = sum(e)
+        for j in range(L):
+            prob[i, j] = e[j] / tot
+            for c in range(v.shape[1]):
+                out[i, c] += prob[i, j] * v[j, c]
+    return out, prob
+
+
+def test_attention_matches_naive_loops():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((5, 8)) * 2
+    k = rng.standard_normal((11, 8)) * 2
+    v = rng.standard_normal((11, 8))
+    o, p, m, l = O.attention_head(q, k, v, 1 / math.sqrt(8))
+    o2, p2 = _naive_attention(q, k, v, 1 / math.sqrt(8))
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(p, p2, rtol=1e-12, atol=1e-15)
+
+
+def test_attention_matches_torch_sdpa_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((2, 9, 16))
+    k = rng.standard_normal((2, 40, 16))
+    v = rng.standard_normal((2, 40, 16))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        is_causal=False)[0].numpy()
+    for h in range(2):
+        o, _, _, _ = O.attention_head(q[h], k[h], v[h], 1 / math.sqrt(16))
+        np.testing.assert_allclose(o, ref[h], rtol=1e-11, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((3, 8))
+    v = rng.standard_normal((6, 8))
+    # one key: output is its value row
+    o, p, _, _ = O.attention_head(q, rng.standard_normal((1, 8)), v[:1], 0.3)
+    np.testing.assert_allclose(o, np.repeat(v[:1], 3, 0), rtol=1e-15)
+    # all keys equal: uniform probabilities, output is the mean value row
+    kk = np.repeat(rng.standard_normal((1, 8)), 6, 0)
+    o, p, _, _ = O.attention_head(q, kk, v, 0.3)
+    np.testing.assert_allclose(p, np.full((3, 6), 1 / 6), rtol=1e-14)
+    np.testing.assert_allclose(o, np.repeat(v.mean(0, keepdims=True), 3, 0), rtol=1e-13, atol=1e-15)
+    # zero query: uniform whatever the keys
+    o, p, _, _ = O.attention_head(np.zeros((2, 8)), rng.standard_normal((6, 8)), v, 0.3)
+    np.testing.assert_allclose(p, np.full((2, 6), 1 / 6), rtol=1e-14)
+
+
+def test_attention_golden_two_keys():
+    g = _golden("attention_two_keys.json")
+    D = g["head_dim"]
+    q = np.array(g["q"]) * g["q_is_scaled_by"]
+    o, p, _, _ = O.attention_head(q, np.array(g["k"]), np.array(g["v"]), 1 / math.sqrt(D))
+    np.testing.assert_allclose(p, g["expected_p"], rtol=1e-15)
+    np.testing.assert_allclose(o, g["expected_o"], rtol=1e-14, atol=1e-15)
+    # through the paged varlen entry: one sequence, one head, page size 2
+    kc = np.array(g["k"], np.float32).reshape(1, 1, 2, D)
+    vc = np.array(g["v"], np.float32).reshape(1, 1, 2, D)
+    out, imp = O.varlen_attention(q.reshape(1, 1, D), O.as_f64(kc, "f32"), O.as_f64(vc, "f32"),
+                                  np.array([[0]]), 2, [0, 1], [0, 2], 1 / math.sqrt(D))
+    np.testing.assert_allclose(imp[0], g["expected_importance"], rtol=1e-15)
+    np.testing.assert_allclose(out[0, 0], g["expected_o"][0], rtol=1e-14, atol=1e-15)
+
+
+def _paged(kv, ps, rng):
+    """Scatter a logical [L, H, D] array into random pages of size ps."""
+    L, H, D = kv.shape
+    n = (L + ps - 1) // ps
+    perm = rng.permutation(n + 3)[:n]
+    cache = np.full((n + 3, H, ps, D), np.nan)
+    for p in range(L):
+        cache[perm[p // ps], :, p % ps] = kv[p]
+    return cache, perm
+
+
+def test_importance_invariants_and_zero_query():
+    rng = np.random.default_rng(10)
+    H, D, ps = 3, 8, 4
+    Ls = [13, 7]
+    Qs = [5, 3]
+    ks = [rng.standard_normal((L, H, D)) for L in Ls]
+    vs = [rng.standard_normal((L, H, D)) for L in Ls]
+    # two sequences, paged separately into one pool
+    pool_k, pool_v, rows = [], [], []
+    table = np.full((2, 4), -1)
+    base = 0
+    for b in range(2):
+        ck, perm = _paged(ks[b], ps, rng)
+        cv = np.full_like(ck, np.nan)
+        for p in range(Ls[b]):
+            cv[perm[p // ps], :, p % ps] = vs[b][p]
+        pool_k.append(ck)
+        pool_v.append(cv)
+        table[b, :len(perm)] = perm + base
+        base += ck.shape[0]
+    kc = np.concatenate(pool_k)
+    vc = np.concatenate(pool_v)
+    cu_q = np.array([0, 5, 8])
+    cu_k = np.array([0, 13, 20])
+    q = rng.standard_normal((8, H, D))
+    out, imp = O.varlen_attention(q, kc, vc, table, ps, cu_q, cu_k, 1 / math.sqrt(D))
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(imp))
+    for b in range(2):
+        for h in range(H):
+            # rows of P sum to one, so a sequence's column sums add up to its query count
+            assert abs(imp[h, cu_k[b]:cu_k[b + 1]].sum() - Qs[b]) < 1e-12
+            o2, p2 = _naive_attention(q[cu_q[b]:cu_q[b + 1], h], ks[b][:, h], vs[b][:, h],
+                                      1 / math.sqrt(D))
+            np.testing.assert_allclose(out[cu_q[b]:cu_q[b + 1], h], o2, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(imp[h, cu_k[b]:cu_k[b + 1]], p2.sum(0), rtol=1e-12)
+    # zero query: every key of sequence b gets Q_b / L_b per head
+    out, imp = O.varlen_attention(np.zeros_like(q), kc, vc, table, ps, cu_q, cu_k, 0.5)
+    for b in range(2):
+        np.testing.assert_allclose(imp[:, cu_k[b]:cu_k[b + 1]], Qs[b] / Ls[b], rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# top-k
+# ---------------------------------------------------------------------------
+
+def test_topk_exhaustive_with_planted_ties():
+    rng = np.random.default_rng(12)
+    for trial in range(300):
+        n = int(rng.integers(1, 10))
+        k = int(rng.integers(1, 12))
+        # few distinct values -> many ties
+        score = rng.integers(0, 4, size=n).astype(np.float64) / 4
+        pos = rng.permutation(40)[:n]
+        got, _ = O.topk_select(score, pos, k)
+        np.testing.assert_array_equal(got, O.topk_exhaustive(score, pos, k))
+        # numpy lexsort: primary key -score, secondary key position
+        order = np.lexsort((pos, -score))[:k]
+        np.testing.assert_array_equal(got, np.sort(pos[order]))
+
+
+def test_topk_golden_ties_and_candidates():
+    g = _golden("topk_ties.json")
+    score = np.array(g["score"])
+    H = 2
+    imp = np.stack([score * 0.25, score * 0.75])      # head sum gives back `score`
+    cand = np.array(g["candidate"], np.uint8)
+    for case in g["cases"]:
+        pos, cnt, sc, _ = O.importance_topk(imp, [0, len(score)], cand, case["k"])
+        n = len(case["expected"])
+        assert cnt[0] == n
+        np.testing.assert_array_equal(pos[0, :n], case["expected"])
+        assert np.all(pos[0, n:] == -1)
+
+
+def test_head_sum_float32_is_sequential_rounding():
+    rng = np.random.default_rng(13)
+    imp = rng.random((32, 50)) * 3
+    s = O.head_sum(imp, as_float32=True)
+    for j in range(50):
+        acc = np.float32(0)
+        for h in range(32):
+            acc = np.float32(acc + np.float32(imp[h, j]))
+        assert s[j] == acc
+
+
+# ---------------------------------------------------------------------------
+# verify
+# ---------------------------------------------------------------------------
+
+def test_argmax_conf_closed_forms():
+    V = 1000
+    a, c = O.argmax_conf(np.zeros(V))
+    assert a == 0 and abs(c - 1 / V) < 1e-15
+    for val in (0.5, 3.0, 9.0):
+        row = np.zeros(V)
+        row[417] = val
+        a, c = O.argmax_conf(row)
+        assert a == 417
+        assert abs(c - math.exp(val) / (math.exp(val) + V - 1)) < 1e-14
+    rng = np.random.default_rng(14)
+    for _ in range(50):
+        row = O.bf16_to_f64(W.to_bf16_bits((rng.standard_normal(300) * 2).astype(np.float32)))
+        row[rng.integers(0, 300, 3)] = row.max()          # planted ties
+        a, _ = O.argmax_conf(row)
+        assert a == int(np.argmax(row))                     # numpy: first occurrence
+
+
+def test_verify_golden_truth_table():
+    g = _golden("verify_truth_table.json")
+    V = g["vocab"]
+    P = g["positions"]
+    n = len(P)
+    rows = [p["draft_view"] for p in P] + [p["mask_view"] for p in P]
+    bits = W.to_bf16_bits(np.array(rows, np.float32))
+    # the fixture's logits are exact in bf16
+    np.testing.assert_array_equal(O.bf16_to_f64(bits), np.array(rows))
+    draft = np.array([p["draft"] for p in P], np.int32)
+    am, conf, acc, acc_pos = O.verify_accept(bits, [0, n], draft, g["tau"])
+    np.testing.assert_array_equal(am[:n], [p["argmax"][0] for p in P])
+    np.testing.assert_array_equal(am[n:], [p["argmax"][1] for p in P])
+    np.testing.assert_allclose(conf[:n], [p["conf"][0] for p in P], rtol=1e-14)
+    np.testing.assert_allclose(conf[n:], [p["conf"][1] for p in P], rtol=1e-14)
+    np.testing.assert_array_equal(acc[:n], [p["accept_row"][0] for p in P])
+    np.testing.assert_array_equal(acc[n:], [p["accept_row"][1] for p in P])
+    np.testing.assert_array_equal(acc_pos, [p["accept_pos"] for p in P])
+    # closed form of the one-hot rows, independent of the fixture numbers
+    for p in P:
+        row = np.array(p["draft_view"])
+        if np.count_nonzero(row) == 1:
+            a = row.max()
+            assert abs(p["conf"][0] - math.exp(a) / (math.exp(a) + V - 1)) < 1e-15
+
+
+def test_verify_two_sequences_row_layout():
+    # sequence 0 has 2 positions, sequence 1 has 1: rows are
+    # [s0 draft p0, s0 draft p1, s0 mask p0, s0 mask p1, s1 draft p0, s1 mask p0]
+    V = 6
+    hot = lambda t: [8.0 if i == t else 0.0 for i in range(V)]
+    rows = [hot(1), hot(2), hot(1), hot(3), hot(5), hot(5)]
+    bits = W.to_bf16_bits(np.array(rows, np.float32))
+    am, conf, acc, acc_pos = O.verify_accept(bits, [0, 2, 3], np.array([1, 2, 5], np.int32), 0.9)
+    np.testing.assert_array_equal(am, [1, 2, 1, 3, 5, 5])
+    np.testing.assert_array_equal(acc, [1, 1, 1, 0, 1, 1])
+    np.testing.assert_array_equal(acc_pos, [1, 0, 1])
+
+
+# ---------------------------------------------------------------------------
+# output projection with residual
+# ---------------------------------------------------------------------------
+
+def test_linear_residual_brute_force():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((3, 5)).astype(np.float32)
+    w = rng.standard_normal((4, 5)).astype(np.float32)
+    h = rng.standard_normal((3, 4)).astype(np.float32)
+    y = O.linear_residual(x, w, h, "f32")
+    for i, j in product(range(3), range(4)):
+        ref = float(h[i, j]) + sum(float(x[i, c]) * float(w[j, c]) for c in range(5))
+        assert abs(y[i, j] - ref) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# a whole step on the tiny fp32 workload
+# ---------------------------------------------------------------------------
+
+def test_tiny_step_chain_properties():
+    from kv_cache_attention_step_amd.configs import C0
+    inp = W.make_step_inputs(C0)
+    r = O.flash_cache_step(inp.hidden, inp.positions, inp.cu_seqlens_q, inp.cu_seqlens_k,
+                           inp.w_qkv, C0.n_heads, C0.head_dim, C0.rope_base, inp.k_cache,
+                           inp.v_cache, inp.block_table, C0.page_size, inp.cand_mask, C0.track,
+                           C0.dtype)
+    assert inp.T_q == 32 and inp.T_k == 128
+    assert r["topk_count"][0] == 16
+    pos = r["topk_pos"][0]
+    assert np.all(np.diff(pos) > 0)
+    assert np.all((pos >= 64) & (pos < 112))
+    # importance: each head's column sums over the sequence add up to Q_b
+    np.testing.assert_allclose(r["importance"].sum(axis=1), 32.0, rtol=1e-12)
+    # the tracked set equals the 16 largest head-summed scores among candidates
+    score = r["importance"].sum(0)
+    cand = np.arange(64, 112)
+    best = cand[np.argsort(-score[cand], kind="stable")[:16]]
+    np.testing.assert_array_equal(pos, np.sort(best))
