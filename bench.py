@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of one Flash-Cache denoising step on one MI355X.
+
+A step is the whole hot path for one layer: fused QKV projection + RoPE +
+paged cache write -> bidirectional varlen attention with fused importance ->
+top-k reselection, on the batched varlen workload (B=32, LLaDA-8B-shaped layer,
+caches of 768..1536 positions, 128 query tokens per sequence). Inputs are seeded
+synthetic data already resident in device memory when timing starts. Between
+steps a 512 MiB buffer is overwritten so that no step finds the previous step's
+weights or cache in the 256 MB Infinity Cache (each layer of a real model has its
+own weights).
+
+Prints ONE JSON line (rank 0). Per-kernel times come from HIP events recorded
+on the stream the kernels run on.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C2")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=32,
+                    help="sequences of the batch the CPU oracle baseline runs")
+    return ap.parse_args()
+
+
+def step_work(inp):
+    """Algorithmic work per step (one layer)."""
+    cfg = inp.cfg
+    T_q, T_k, d, H, D = inp.T_q, inp.T_k, cfg.d_model, cfg.n_heads, cfg.head_dim
+    esz = 2 if cfg.dtype == "bf16" else 4
+    qkv_flops = 2.0 * T_q * (3 * d) * d
+    qkv_bytes = (T_q * d + 3 * d * d + 3 * T_q * d) * esz + T_q * 8   # in, W, q/k/v out, pos+slot
+    kv_bytes = 2.0 * T_k * H * D * esz                                 # K and V once
+    attn_bytes = kv_bytes + 2.0 * T_q * d * esz + H * T_k * 4.0        # + Q + O + importance
+    attn_flops = sum(4.0 * (int(inp.cu_seqlens_q[b + 1] - inp.cu_seqlens_q[b])) *
+                     int(inp.cu_seqlens_k[b + 1] - inp.cu_seqlens_k[b]) * D * H
+                     for b in range(inp.B))
+    topk_bytes = H * T_k * 4.0 + T_k
+    return dict(qkv_flops=qkv_flops, qkv_bytes=qkv_bytes, attn_bytes=attn_bytes,
+                attn_flops=attn_flops, topk_bytes=topk_bytes)
+
+
+def cpu_baseline(inp, n_seqs, budget_s=12.0):
+    """The oracle, untuned, on the leading sequences of the same batch: at most
+    n_seqs of them, stopping once budget_s seconds of CPU work are spent."""
+    import numpy as np
+    from kv_cache_attention_step_amd.workload import sequence_inputs
+    from oracle import flashcache_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = inp.cfg
+    n = min(n_seqs, inp.B)
+    tokens = 0
+    t0 = time.perf_counter()
+    for b in range(n):
+        s = sequence_inputs(inp, b)
+        O.flash_cache_step(s["hidden"], s["positions"], s["cu_q"], s["cu_k"], inp.w_qkv,
+                           cfg.n_heads, cfg.head_dim, cfg.rope_base, s["k_cache"], s["v_cache"],
+                           s["block_table"], cfg.page_size, s["cand"], cfg.track, cfg.dtype)
+        tokens += s["q1"] - s["q0"]
+        if time.perf_counter() - t0 >= budget_s:
+            n = b + 1
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "query-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} of {inp.B} sequences of the same batch ({tokens} query tokens), "
+                      f"full step each (fp64 projection, RoPE, cache write, attention, "
+                      f"importance, top-k); {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd import workload as W
+    from kv_cache_attention_step_amd.runner import StepBuffers
+
+    cfg = CF.CONFIGS[args.config]
+    inp = W.make_step_inputs(cfg)
+    torch.cuda.set_device(0)
+    bufs = StepBuffers(inp, device="cuda:0")
+    stream = torch.cuda.Stream()
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+
+    def one_step(ev=None):
+        if flush is not None:
+            with torch.cuda.stream(stream):
+                flush.fill_(1)
+        if ev is not None:
+            ev[0].record(stream)
+        bufs.qkv(stream)
+        if ev is not None:
+            ev[1].record(stream)
+        bufs.attention(stream)
+        if ev is not None:
+            ev[2].record(stream)
+        bufs.topk(stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1 = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    k2 = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    k3 = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    ms_per_step = float(step_ms.mean())
+    work = step_work(inp)
+    k1_us, k2_us, k3_us = float(k1.mean()) * 1e3, float(k2.mean()) * 1e3, float(k3.mean()) * 1e3
+    kernels = {
+        "qkv_rope_cache_write": {
+            "avg_us": round(k1_us, 2), "bound": "mfma",
+            "achieved_tflops": round(work["qkv_flops"] / (k1_us * 1e-6) / 1e12, 1),
+            "frac": round(work["qkv_flops"] / (k1_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "varlen_bidir_attention": {
+            "avg_us": round(k2_us, 2), "bound": "hbm",
+            "achieved_gbs": round(work["attn_bytes"] / (k2_us * 1e-6) / 1e9, 1),
+            "frac": round(work["attn_bytes"] / (k2_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "importance_topk": {
+            "avg_us": round(k3_us, 2), "bound": "hbm",
+            "achieved_gbs": round(work["topk_bytes"] / (k3_us * 1e-6) / 1e9, 1),
+            "frac": round(work["topk_bytes"] / (k3_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    kd = kernels[dominant]
+    if kd["bound"] == "mfma":
+        roof = {"bound": "mfma", "kernel": dominant, "achieved": kd["achieved_tflops"],
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kd["frac"],
+                "traffic": None}
+    else:
+        roof = {"bound": "hbm", "kernel": dominant, "achieved": kd["achieved_gbs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["frac"], "traffic": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_seqs)
+    L = inp.cache_len
+    out = {
+        "metric": "Flash-Cache step query-tokens/s at B=32 + % of HBM/MFMA roofline (1 GPU)",
+        "value": round(inp.T_q / (ms_per_step * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic: seeded N(0,1) hidden states, N(0,0.02) Wqkv, N(0,1.28) stale "
+                "KV cache, random page tables; no trained weights or datasets",
+        "config": {"workload": f"{cfg.name}: one Flash-Cache step of one layer (QKV+RoPE+paged "
+                               f"cache write, bidirectional varlen attention + importance, "
+                               f"top-k)",
+                   "batch": inp.B, "d_model": cfg.d_model, "heads": cfg.n_heads,
+                   "head_dim": cfg.head_dim, "query_tokens": inp.T_q,
+                   "query_per_seq": f"{cfg.window} window + {cfg.track} tracked",
+                   "cache_tokens": inp.T_k, "cache_len_range": [int(L.min()), int(L.max())],
+                   "page_size": cfg.page_size, "infinity_cache_flushed": flush is not None},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "step_ms_min": round(float(step_ms.min()), 4),
+        "wall_s_timed_loop": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

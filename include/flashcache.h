@@ -1,0 +1,230 @@
+/*
+ * flashcache.h -- C ABI of libflashcache.so: the Flash-Cache denoising step of
+ * Flash-dLLM (arXiv 2609.26796) as hand-written HIP kernels for AMD CDNA4
+ * (gfx950, MI355X).
+ *
+ * Method sources (web pages about Flash-dLLM):
+ *   [FIG]    signal-papers page on arXiv 2609.26796, figure captions, Fig. 2:
+ *            each step a fixed-size query of beta_m tokens (tracked positions +
+ *            the current masked window) attends bidirectionally to the full KV
+ *            cache through the fused kernel; tracked positions are the top-k
+ *            decoded tokens by attention importance.
+ *   [NEWS]   infernews post "Flash-dLLM 讓擴散式語言模型解碼更快、更省記憶體",
+ *            paragraph 2: one fused kernel does the QKV projection, RoPE and the
+ *            cache writes; block-scheduled attention serves different query
+ *            lengths in one batch; only new tokens and a few positions chosen by
+ *            attention importance are refreshed. Paragraph 3: Flash-Verify checks
+ *            drafts and [MASK] tokens through two views and accepts together
+ *            the predictions that meet a confidence threshold.
+ *   [README] zhichai.net forum post quoting the project README, section 4:
+ *            defaults block length 16, confidence threshold 0.9.
+ *
+ * Conventions for every entry point
+ *   - Pointers are device pointers owned by the caller (for example torch
+ *     tensors). The library keeps no pointer after the call returns, never
+ *     frees caller memory, and allocates no device memory.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without waiting; inputs must stay valid and unchanged until the
+ *     stream has run the work. Faults inside a kernel show up at the caller's
+ *     next synchronisation, as with any HIP launch.
+ *   - Arguments are checked on the host before anything is enqueued; a failed
+ *     check returns an error status and enqueues nothing. fc_last_error()
+ *     gives a readable message for the calling thread's last failure.
+ *   - Arrays are row-major and densely packed. Indices are int32.
+ *   - Calls keep no state between them; calls on different streams with
+ *     disjoint outputs may run concurrently.
+ *   - dtype: FC_DTYPE_BF16 (bf16 storage, fp32 accumulation) or FC_DTYPE_F32.
+ *
+ * Notation: B sequences; sequence b has query length Q_b (its rows are packed
+ * by cu_seqlens_q) and cache length L_b (cu_seqlens_k); H heads of size D;
+ * d = H * D; T_q = sum Q_b, T_k = sum L_b. cu_seqlens_* are [B+1] exclusive
+ * prefix sums starting at 0.
+ *
+ * Paged KV cache: k_cache and v_cache are [num_pages, H, page_size, D]. Cache
+ * position p of sequence b lives in page block_table[b * max_pages_per_seq +
+ * p / page_size] at offset p % page_size; its slot id is
+ * page * page_size + offset.
+ */
+#ifndef FLASHCACHE_H
+#define FLASHCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* fc_stream_t;   /* a hipStream_t */
+
+typedef enum {
+  FC_OK = 0,
+  FC_ERR_INVALID_VALUE = 1,   /* null pointer, negative or inconsistent size    */
+  FC_ERR_UNSUPPORTED = 2,     /* valid request that this build does not handle  */
+  FC_ERR_WORKSPACE = 3,       /* workspace missing or smaller than required     */
+  FC_ERR_HIP = 4              /* a HIP runtime call failed (message has detail) */
+} fc_status_t;
+
+enum { FC_DTYPE_F32 = 0, FC_DTYPE_BF16 = 1 };
+
+/* Static description of a status code. Never NULL. */
+const char* fc_status_string(fc_status_t status);
+
+/* Message for the calling thread's most recent failed call ("" if none).
+ * Valid until the thread's next call into the library. Never NULL. */
+const char* fc_last_error(void);
+
+/* Library version string, e.g. "flashcache-gfx950 0.1". */
+const char* fc_version(void);
+
+/*
+ * Fused QKV projection + RoPE + paged cache write ([NEWS] paragraph 2; the
+ * query and its tokens: [FIG] Fig. 2).
+ *
+ * For every query token t (row t of hidden, sequence b, position positions[t]):
+ *   [q k v] = hidden[t] . w_qkv^T            (fp32 accumulation)
+ *   q, k   <- rotate-half RoPE at positions[t]: for e < D/2, the pair
+ *             (x_e, x_{e+D/2}) turns by angle positions[t] * rope_base^(-2e/D):
+ *             x_e' = x_e cos - x_{e+D/2} sin,  x_{e+D/2}' = x_{e+D/2} cos + x_e sin
+ *   q_out[t]               = q (rounded to dtype)
+ *   k_cache/v_cache at the slot of (b, positions[t]) = k / v (rounded to dtype)
+ *   slot_mapping[t]        = that slot id
+ *
+ * hidden        [T_q, d]            dtype
+ * positions     [T_q]               cache position of each token, 0 <= p < L_b;
+ *                                   distinct within a sequence when the cache is
+ *                                   written (two tokens on one slot would race)
+ * cu_seqlens_q  [B+1]               token rows per sequence
+ * T_q                               total query tokens (= cu_seqlens_q[B])
+ * w_qkv         [3d, d]             dtype; rows are the Q, K, V blocks, each
+ *                                   head-major (row h*D + e of a block); no bias
+ * k_cache, v_cache                  dtype, written in place; both NULL for a
+ *                                   projection that writes no cache (the verify
+ *                                   pass, where two views share positions)
+ * block_table   [B, max_pages_per_seq]   page ids (entries past the last page
+ *                                   of a sequence are never read)
+ * q_out         [T_q, H, D]         dtype
+ * slot_mapping  [T_q] or NULL
+ * Supported: bf16 with D = 128 and d a multiple of 256; f32 with D in {64,128}.
+ * page_size must be a power of two in [1, 256].
+ */
+fc_status_t fc_qkv_rope_cache_write(
+    const void* hidden, const int32_t* positions, const int32_t* cu_seqlens_q, int32_t B,
+    int32_t T_q, const void* w_qkv, int32_t d_model, int32_t n_heads, int32_t head_dim,
+    float rope_base, void* k_cache, void* v_cache, const int32_t* block_table,
+    int32_t max_pages_per_seq, int32_t page_size, void* q_out, int32_t* slot_mapping,
+    int32_t dtype, fc_stream_t stream);
+
+/* Bytes of device workspace fc_varlen_bidir_attention needs for these sizes
+ * (0 when none). */
+size_t fc_attention_workspace_size(int32_t B, int32_t T_q, int32_t T_k, int32_t n_heads,
+                                   int32_t head_dim, int32_t with_importance);
+
+/*
+ * Bidirectional varlen attention over each sequence's whole paged cache, with
+ * the per-key attention importance fused in ([FIG] Fig. 2: no causal mask,
+ * every cached key; [NEWS] paragraph 2: block-scheduled attention across
+ * sequences of different query lengths, importance picks refreshed positions).
+ *
+ * For sequence b, head h and query row i of b:
+ *   s_ij = softmax_scale * <q[i, h], k_j>      over all keys j < L_b of b
+ *   P_ij = exp(s_ij - max_j s_ij) / sum_j exp(s_ij - max_j s_ij)
+ *   out[i, h] = sum_j P_ij v_j
+ * and, when importance != NULL, for every key j of b:
+ *   importance[h, cu_seqlens_k[b] + j]  (=, or += when accumulate) sum_i P_ij
+ * The importance path computes exact normalised P in two passes over the keys
+ * (row max and normaliser first), so it reads K twice. With importance == NULL
+ * a single online-softmax pass is used.
+ *
+ * q             [T_q, H, D]  dtype (post-RoPE queries)
+ * k_cache, v_cache, block_table, page_size   the paged cache (see above)
+ * max_seqlen_q                max Q_b (sizes the grid; rows beyond Q_b idle)
+ * out           [T_q, H, D]  dtype
+ * importance    [H, T_k] fp32 or NULL
+ * workspace     device memory of fc_attention_workspace_size() bytes, or NULL
+ *               when that size is 0
+ * A sequence with L_b = 0 gets out = 0. Supported: bf16 with D = 128; f32 with
+ * D in {64, 128}.
+ */
+fc_status_t fc_varlen_bidir_attention(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+    int32_t max_pages_per_seq, int32_t page_size, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, int32_t B, int32_t max_seqlen_q, int32_t T_k, int32_t n_heads,
+    int32_t head_dim, float softmax_scale, void* out, float* importance, int32_t accumulate,
+    void* workspace, size_t workspace_bytes, int32_t dtype, fc_stream_t stream);
+
+/*
+ * Top-k reselection of the tracked positions ([FIG] Fig. 2: tracked positions
+ * are the top-k decoded tokens by attention importance).
+ *
+ * score_j = sum over h = 0..H-1, in that order, of importance[h, j] (fp32).
+ * For each sequence b, among its candidate positions (candidate_mask != 0, or
+ * all positions when candidate_mask is NULL) keep min(k, #candidates) of them:
+ * larger score first, equal scores -> lower position.
+ *
+ * importance      [H, T_k] fp32
+ * candidate_mask  [T_k] uint8 or NULL
+ * topk_pos        [B, k] chosen positions (within the sequence) in ascending
+ *                 order, -1 after the last one
+ * topk_count      [B] number chosen; -1 if L_b exceeds FC_TOPK_MAX_LEN (that
+ *                 sequence's row is then left as all -1)
+ * topk_score      [B, k] fp32 scores in the same order (NaN padded) or NULL
+ */
+#define FC_TOPK_MAX_LEN 16384
+fc_status_t fc_importance_topk(
+    const float* importance, const int32_t* cu_seqlens_k, int32_t B, int32_t T_k,
+    int32_t n_heads, const uint8_t* candidate_mask, int32_t k, int32_t* topk_pos,
+    int32_t* topk_count, float* topk_score, fc_stream_t stream);
+
+/*
+ * Flash-Verify accept test over the draft and [MASK] views ([NEWS] paragraph 3;
+ * threshold default 0.9 from [README] section 4).
+ *
+ * Rows: sequence b owns n_b = cu_positions[b+1] - cu_positions[b] verified
+ * positions and 2 n_b logit rows starting at row 2*cu_positions[b]: first the
+ * n_b draft-view rows, then the n_b mask-view rows, both in position order.
+ * For row r of verified position p:
+ *   argmax[r]     = lowest token id among the row's maxima
+ *   conf[r]       = 1 / sum_v exp(logits[r, v] - logits[r, argmax[r]])
+ *                   (the largest softmax probability), fp32
+ *   accept_row[r] = argmax[r] == draft_tokens[p]  and  conf[r] >= tau
+ *   accept_pos[p] = accept_row[draft-view row] and accept_row[mask-view row]
+ *
+ * logits        [R, vocab] bf16, R = 2 * cu_positions[B]
+ * cu_positions  [B+1]
+ * draft_tokens  [cu_positions[B]] int32
+ * tau           confidence threshold in (0, 1], compared as fp32, inclusive
+ * argmax [R] int32, conf [R] fp32, accept_row [R] uint8; accept_pos
+ * [cu_positions[B]] uint8 or NULL.
+ */
+fc_status_t fv_verify_accept(
+    const void* logits, int32_t vocab, const int32_t* cu_positions, int32_t B, int32_t R,
+    const int32_t* draft_tokens, float tau, int32_t* argmax, float* conf, uint8_t* accept_row,
+    uint8_t* accept_pos, fc_stream_t stream);
+
+/*
+ * Output projection with residual for the layer stack: h_inout += x . w^T
+ * (fp32 accumulation, one rounding to dtype).
+ * x [M, K], w [N, K], h_inout [M, N], all dtype. Supported: bf16 with N a
+ * multiple of 128 and K a multiple of 64; f32 any size.
+ */
+fc_status_t fc_linear_residual(const void* x, const void* w, void* h_inout, int32_t M,
+                               int32_t N, int32_t K, int32_t dtype, fc_stream_t stream);
+
+/*
+ * Query assembly for the next denoising step ([FIG] Fig. 2: the query is the
+ * tracked positions plus the current masked window).
+ * For sequence b, rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of positions get
+ * the first topk_count[b] entries of topk_pos[b] followed by window_start[b],
+ * window_start[b]+1, ... (up to the sequence's query length). topk_pos/count
+ * may be NULL (window only). topk_pos is [B, k].
+ */
+fc_status_t fc_assemble_query(const int32_t* topk_pos, const int32_t* topk_count, int32_t k,
+                              const int32_t* window_start, const int32_t* cu_seqlens_q,
+                              int32_t B, int32_t* positions, fc_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHCACHE_H */

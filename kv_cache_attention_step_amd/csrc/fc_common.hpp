@@ -1,0 +1,64 @@
+// Shared device/host helpers for the gfx950 kernels of libflashcache.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/flashcache.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define FC_DEVICE __device__ __forceinline__
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (bf16 is the upper half of an fp32)
+// ---------------------------------------------------------------------------
+FC_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+FC_DEVICE float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+FC_DEVICE float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// round to nearest even; NaN stays NaN
+FC_DEVICE uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+FC_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// MFMA wrappers: D = A * B + C with A [32 x 16] (lane l: row l%32, k = 8*(l/32)..+7),
+// B [16 x 32] (lane l: column l%32, same k), C/D [32 x 32] (lane l: column l%32,
+// register i: row 8*(i/4) + 4*(l/32) + i%4).
+FC_DEVICE f32x16_t mfma32x32x16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Raw buffer descriptor over [base, base + bytes): loads past the end return 0.
+FC_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+FC_DEVICE bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// ---------------------------------------------------------------------------
+// host-side error plumbing (fc_status.cpp)
+// ---------------------------------------------------------------------------
+fc_status_t fc_fail(fc_status_t st, const char* fmt, ...);
+fc_status_t fc_check_launch(const char* what);
+void fc_clear_error();
+
+#define FC_REQUIRE(cond, st, ...)                   \
+  do {                                              \
+    if (!(cond)) return fc_fail((st), __VA_ARGS__); \
+  } while (0)
+
+static inline bool fc_is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+static inline int fc_log2i(int x) { int r = 0; while ((1 << r) < x) ++r; return r; }

@@ -1,0 +1,236 @@
+// Fused QKV projection + RoPE + paged KV-cache write (one pass, one launch).
+//
+// The Flash-Cache kernel projects the step's query tokens to Q, K and V, rotates
+// Q and K with RoPE and writes K and V into the cache in a single pass
+// (infernews post "Flash-dLLM 讓擴散式語言模型解碼更快、更省記憶體", paragraph 2).
+//
+// bf16 path: a 256 x 256 x 64 MFMA GEMM tile (gemm_tile.hpp) whose epilogue works
+// on the fp32 accumulators in registers. Each wave owns 128 output columns, i.e.
+// exactly one head of D = 128, so the rotate-half partners e and e + 64 of a
+// token sit in the same lane and register index of accumulator blocks nb and
+// nb + 2: RoPE needs no data exchange. Rotation angles are formed in fp64 as
+// revolutions (pos * base^(-2e/D) / 2pi, fractional part) and fed to the
+// hardware sine/cosine, which take revolutions. Rounded bf16 values go straight
+// to q_out or to the token's cache slot.
+//
+// f32 path (small models): one work-item per (token, head, rotation pair).
+#include "gemm_tile.hpp"
+
+#include <math.h>
+
+namespace {
+
+constexpr int QKV_BM = 256, QKV_BN = 256;
+
+FC_DEVICE int find_seq(const int32_t* __restrict__ cu, int B, int row) {
+  int lo = 0, hi = B;  // invariant: cu[lo] <= row < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256, 1) void qkv_rope_cache_bf16_d128(
+    const uint16_t* __restrict__ hidden, const int32_t* __restrict__ positions,
+    const int32_t* __restrict__ cu_q, int B, int M, const uint16_t* __restrict__ w, int d, int H,
+    float rope_base, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ block_table, int maxp, int log2ps, uint16_t* __restrict__ q_out,
+    int32_t* __restrict__ slot_mapping, int n_tiles_n) {
+  using ML = GemmMainloop<QKV_BM, QKV_BN>;
+  using C = ML::C;
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+
+  // N-tile fastest: consecutive workgroups (spread over the XCDs round-robin)
+  // take different weight column blocks, so each XCD streams a disjoint slice of W.
+  const int nt = blockIdx.x % n_tiles_n;
+  const int mt = blockIdx.x / n_tiles_n;
+  const int m0 = mt * QKV_BM, n0 = nt * QKV_BN;
+
+  f32x16_t acc[C::MB][C::NB];
+  ML::run(hidden, d, M, w, d, 3 * d, d, m0, n0, lds, acc);
+
+  // token positions and cache slots of this tile's rows
+  int* s_pos = (int*)lds;
+  int* s_slot = s_pos + QKV_BM;
+  const int t = threadIdx.x;
+  const int ps_mask = (1 << log2ps) - 1;
+  {
+    const int row = m0 + t;
+    int p = 0, slot = 0;
+    if (row < M) {
+      p = positions[row];
+      if (block_table) {
+        const int b = find_seq(cu_q, B, row);
+        const int page = block_table[(size_t)b * maxp + (p >> log2ps)];
+        slot = (page << log2ps) + (p & ps_mask);
+        if (nt == 0 && slot_mapping) slot_mapping[row] = slot;
+      }
+    }
+    s_pos[t] = p;
+    s_slot[t] = slot;
+  }
+  __syncthreads();
+
+  const int wave = t >> 6, lane = t & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int col0 = n0 + wn * C::WN;
+  const int region = col0 / d;              // 0 = Q, 1 = K, 2 = V
+  const int h = (col0 - region * d) / D;
+
+  if (region < 2) {
+    double frev[2];
+    const double l2b = log2((double)rope_base);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int e = nb * 32 + (lane & 31);
+      frev[nb] = exp2(-2.0 * (double)e / (double)D * l2b) * 0.15915494309189535;  // / 2pi
+    }
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int pos = s_pos[wm * C::WM + acc_row(mb, i, lane)];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          double r = (double)pos * frev[nb];
+          r -= floor(r);
+          const float rf = (float)r;
+          const float cs = __builtin_amdgcn_cosf(rf), sn = __builtin_amdgcn_sinf(rf);
+          const float x = acc[mb][nb][i], y = acc[mb][nb + 2][i];
+          acc[mb][nb][i] = x * cs - y * sn;
+          acc[mb][nb + 2][i] = y * cs + x * sn;
+        }
+      }
+  }
+
+  uint16_t* cache = region == 1 ? kc : vc;
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rl = wm * C::WM + acc_row(mb, i, lane);
+      const int row = m0 + rl;
+      if (row >= M) continue;
+      uint16_t* dst;
+      if (region == 0) {
+        dst = q_out + ((size_t)row * H + h) * D;
+      } else {
+        const int slot = s_slot[rl];
+        dst = cache + (((size_t)(slot >> log2ps) * H + h) * (ps_mask + 1) + (slot & ps_mask)) * D;
+      }
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) dst[acc_col(nb, lane)] = f32_to_bf16(acc[mb][nb][i]);
+    }
+}
+
+// fp32: block = (token, region*H + head), D/2 threads, thread e computes the
+// rotation pair (e, e + D/2) of its head.
+__global__ void qkv_rope_cache_f32(const float* __restrict__ hidden,
+                                   const int32_t* __restrict__ positions,
+                                   const int32_t* __restrict__ cu_q, int B,
+                                   const float* __restrict__ w, int d, int H, int D,
+                                   float rope_base, float* __restrict__ kc, float* __restrict__ vc,
+                                   const int32_t* __restrict__ block_table, int maxp, int log2ps,
+                                   float* __restrict__ q_out, int32_t* __restrict__ slot_mapping) {
+  const int row = blockIdx.x;
+  const int region = blockIdx.y / H;
+  const int h = blockIdx.y % H;
+  const int half = D / 2;
+  const int e = threadIdx.x;
+  const float* x = hidden + (size_t)row * d;
+  const float* w0 = w + ((size_t)region * d + h * D + e) * d;
+  const float* w1 = w0 + (size_t)half * d;
+  float a0 = 0.f, a1 = 0.f;
+  for (int c = 0; c < d; ++c) {
+    const float xv = x[c];
+    a0 = fmaf(xv, w0[c], a0);
+    a1 = fmaf(xv, w1[c], a1);
+  }
+  const int p = positions[row];
+  if (region < 2) {
+    const double th = (double)p * exp2(-2.0 * (double)e / (double)D * log2((double)rope_base));
+    double sn, cs;
+    sincos(th, &sn, &cs);
+    const float c = (float)cs, s = (float)sn;
+    const float r0 = a0 * c - a1 * s, r1 = a1 * c + a0 * s;
+    a0 = r0;
+    a1 = r1;
+  }
+  const int ps_mask = (1 << log2ps) - 1;
+  int slot = 0;
+  if (block_table) {
+    const int b = find_seq(cu_q, B, row);
+    slot = (block_table[(size_t)b * maxp + (p >> log2ps)] << log2ps) + (p & ps_mask);
+    if (region == 0 && h == 0 && e == 0 && slot_mapping) slot_mapping[row] = slot;
+  }
+  float* dst;
+  if (region == 0) {
+    dst = q_out + ((size_t)row * H + h) * D;
+  } else {
+    float* cache = region == 1 ? kc : vc;
+    dst = cache + (((size_t)(slot >> log2ps) * H + h) * (ps_mask + 1) + (slot & ps_mask)) * D;
+  }
+  dst[e] = a0;
+  dst[e + half] = a1;
+}
+
+}  // namespace
+
+extern "C" fc_status_t fc_qkv_rope_cache_write(
+    const void* hidden, const int32_t* positions, const int32_t* cu_seqlens_q, int32_t B,
+    int32_t T_q, const void* w_qkv, int32_t d_model, int32_t n_heads, int32_t head_dim,
+    float rope_base, void* k_cache, void* v_cache, const int32_t* block_table,
+    int32_t max_pages_per_seq, int32_t page_size, void* q_out, int32_t* slot_mapping,
+    int32_t dtype, fc_stream_t stream) {
+  fc_clear_error();
+  FC_REQUIRE(B >= 1, FC_ERR_INVALID_VALUE, "fc_qkv_rope_cache_write: B=%d must be >= 1", B);
+  FC_REQUIRE(T_q >= 0, FC_ERR_INVALID_VALUE, "fc_qkv_rope_cache_write: T_q=%d < 0", T_q);
+  FC_REQUIRE(n_heads >= 1 && head_dim >= 2 && d_model == n_heads * head_dim, FC_ERR_INVALID_VALUE,
+             "fc_qkv_rope_cache_write: d_model=%d must equal n_heads=%d * head_dim=%d", d_model,
+             n_heads, head_dim);
+  FC_REQUIRE(dtype == FC_DTYPE_BF16 || dtype == FC_DTYPE_F32, FC_ERR_INVALID_VALUE,
+             "fc_qkv_rope_cache_write: unknown dtype %d", dtype);
+  FC_REQUIRE(rope_base > 1.0f, FC_ERR_INVALID_VALUE, "fc_qkv_rope_cache_write: rope_base %g <= 1",
+             (double)rope_base);
+  FC_REQUIRE((k_cache == nullptr) == (v_cache == nullptr), FC_ERR_INVALID_VALUE,
+             "fc_qkv_rope_cache_write: k_cache and v_cache must both be set or both NULL");
+  const bool write_cache = k_cache != nullptr;
+  if (T_q == 0) return FC_OK;
+  FC_REQUIRE(hidden && positions && cu_seqlens_q && w_qkv && q_out, FC_ERR_INVALID_VALUE,
+             "fc_qkv_rope_cache_write: NULL required pointer");
+  FC_REQUIRE(!write_cache || block_table, FC_ERR_INVALID_VALUE,
+             "fc_qkv_rope_cache_write: block_table required when writing the cache");
+  FC_REQUIRE(!block_table || (max_pages_per_seq >= 1 && fc_is_pow2(page_size) && page_size <= 256),
+             FC_ERR_INVALID_VALUE,
+             "fc_qkv_rope_cache_write: page_size=%d must be a power of two <= 256, "
+             "max_pages_per_seq=%d >= 1", page_size, max_pages_per_seq);
+  const int log2ps = block_table ? fc_log2i(page_size) : 0;
+  hipStream_t st = (hipStream_t)stream;
+
+  if (dtype == FC_DTYPE_BF16) {
+    FC_REQUIRE(head_dim == 128 && d_model % 256 == 0, FC_ERR_UNSUPPORTED,
+               "fc_qkv_rope_cache_write: bf16 needs head_dim 128 and d_model %% 256 == 0 "
+               "(got %d, %d)", head_dim, d_model);
+    FC_REQUIRE((int64_t)T_q * d_model * 2 < (1ll << 31) &&
+                   (int64_t)3 * d_model * d_model * 2 < (1ll << 31),
+               FC_ERR_UNSUPPORTED, "fc_qkv_rope_cache_write: operands above 2 GiB");
+    const int n_tiles_n = (write_cache ? 3 * d_model : d_model) / QKV_BN;
+    const int n_tiles_m = (T_q + QKV_BM - 1) / QKV_BM;
+    hipLaunchKernelGGL(qkv_rope_cache_bf16_d128, dim3(n_tiles_m * n_tiles_n), dim3(256), 0, st,
+                       (const uint16_t*)hidden, positions, cu_seqlens_q, B, T_q,
+                       (const uint16_t*)w_qkv, d_model, n_heads, rope_base, (uint16_t*)k_cache,
+                       (uint16_t*)v_cache, block_table, max_pages_per_seq, log2ps,
+                       (uint16_t*)q_out, slot_mapping, n_tiles_n);
+    return fc_check_launch("fc_qkv_rope_cache_write");
+  }
+  FC_REQUIRE(head_dim == 64 || head_dim == 128, FC_ERR_UNSUPPORTED,
+             "fc_qkv_rope_cache_write: f32 needs head_dim 64 or 128 (got %d)", head_dim);
+  hipLaunchKernelGGL(qkv_rope_cache_f32, dim3(T_q, (write_cache ? 3 : 1) * n_heads),
+                     dim3(head_dim / 2), 0, st, (const float*)hidden, positions, cu_seqlens_q, B,
+                     (const float*)w_qkv, d_model, n_heads, head_dim, rope_base, (float*)k_cache,
+                     (float*)v_cache, block_table, max_pages_per_seq, log2ps, (float*)q_out,
+                     slot_mapping);
+  return fc_check_launch("fc_qkv_rope_cache_write");
+}

@@ -1,0 +1,167 @@
+"""Device-side drivers for the Flash-Cache step built on the C ABI.
+
+Torch provides device memory and streams only; every step of the path runs in
+the library's HIP kernels. Used by the benchmark, the smoke check and the GPU
+tests.
+"""
+import math
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import flashcache as fc
+from .configs import StepConfig
+from .workload import StepInputs, VerifyInputs
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(arr: np.ndarray, device="cuda"):
+    """numpy -> device tensor; bf16 bit patterns travel as int16."""
+    torch = _torch()
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint8:
+        pass
+    return torch.from_numpy(a).to(device)
+
+
+def to_host(t, like: Optional[str] = None) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    return a
+
+
+def dtype_code(dtype: str) -> int:
+    return fc.FC_DTYPE_BF16 if dtype == "bf16" else fc.FC_DTYPE_F32
+
+
+def elem_dtype(dtype: str):
+    torch = _torch()
+    return torch.int16 if dtype == "bf16" else torch.float32
+
+
+class StepBuffers:
+    """Device copies of one step's inputs plus its output buffers."""
+
+    def __init__(self, inp: StepInputs, device="cuda"):
+        torch = _torch()
+        cfg = inp.cfg
+        self.inp = inp
+        self.cfg = cfg
+        self.device = device
+        self.B = inp.B
+        self.T_q = inp.T_q
+        self.T_k = inp.T_k
+        self.H, self.D, self.d = cfg.n_heads, cfg.head_dim, cfg.d_model
+        self.dtype = dtype_code(inp.dtype)
+        self.hidden = to_device(inp.hidden, device)
+        self.positions = to_device(inp.positions, device)
+        self.cu_q = to_device(inp.cu_seqlens_q, device)
+        self.cu_k = to_device(inp.cu_seqlens_k, device)
+        self.w_qkv = to_device(inp.w_qkv, device)
+        self.k_cache = to_device(inp.k_cache, device)
+        self.v_cache = to_device(inp.v_cache, device)
+        self.block_table = to_device(inp.block_table, device)
+        self.cand_mask = to_device(inp.cand_mask, device)
+        et = elem_dtype(inp.dtype)
+        self.q_out = torch.empty((self.T_q, self.H, self.D), dtype=et, device=device)
+        self.attn_out = torch.empty((self.T_q, self.H, self.D), dtype=et, device=device)
+        self.slot_mapping = torch.empty(self.T_q, dtype=torch.int32, device=device)
+        self.importance = torch.empty((self.H, self.T_k), dtype=torch.float32, device=device)
+        k = max(1, cfg.track)
+        self.k = k
+        self.topk_pos = torch.empty((self.B, k), dtype=torch.int32, device=device)
+        self.topk_count = torch.empty(self.B, dtype=torch.int32, device=device)
+        self.topk_score = torch.empty((self.B, k), dtype=torch.float32, device=device)
+        ws = fc.fc_attention_workspace_size(self.B, self.T_q, self.T_k, self.H, self.D, 1)
+        self.ws_bytes = ws
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws else None
+        self.max_seqlen_q = inp.max_seqlen_q
+        self.scale = 1.0 / math.sqrt(self.D)
+
+    # the three calls of one Flash-Cache step
+    def qkv(self, stream=None):
+        cfg = self.cfg
+        fc.fc_qkv_rope_cache_write(self.hidden, self.positions, self.cu_q, self.B, self.T_q,
+                                   self.w_qkv, self.d, self.H, self.D, cfg.rope_base, self.k_cache,
+                                   self.v_cache, self.block_table, self.inp.max_pages,
+                                   cfg.page_size, self.q_out, self.slot_mapping, self.dtype, stream)
+
+    def attention(self, stream=None, importance=True, accumulate=False):
+        fc.fc_varlen_bidir_attention(self.q_out, self.k_cache, self.v_cache, self.block_table,
+                                     self.inp.max_pages, self.cfg.page_size, self.cu_q, self.cu_k,
+                                     self.B, self.max_seqlen_q, self.T_k, self.H, self.D,
+                                     self.scale, self.attn_out,
+                                     self.importance if importance else None, accumulate,
+                                     self.workspace, self.ws_bytes, self.dtype, stream)
+
+    def topk(self, stream=None):
+        fc.fc_importance_topk(self.importance, self.cu_k, self.B, self.T_k, self.H, self.cand_mask,
+                              self.k, self.topk_pos, self.topk_count, self.topk_score, stream)
+
+    def run(self, stream=None):
+        self.qkv(stream)
+        self.attention(stream)
+        self.topk(stream)
+
+    def fetch(self) -> Dict[str, np.ndarray]:
+        return dict(q_out=to_host(self.q_out), attn_out=to_host(self.attn_out),
+                    slot_mapping=to_host(self.slot_mapping), importance=to_host(self.importance),
+                    topk_pos=to_host(self.topk_pos), topk_count=to_host(self.topk_count),
+                    topk_score=to_host(self.topk_score), k_cache=to_host(self.k_cache),
+                    v_cache=to_host(self.v_cache))
+
+
+class VerifyBuffers:
+    """Flash-Verify-shaped step: Q-only projection of both views, one-pass
+    attention over the cache, then the accept test on the logits."""
+
+    def __init__(self, vi: VerifyInputs, device="cuda"):
+        torch = _torch()
+        self.vi = vi
+        self.step = StepBuffers(vi.step, device)
+        cfg = vi.cfg
+        self.V = cfg.vocab
+        self.tau = cfg.tau
+        self.R = 2 * int(vi.cu_positions[-1])
+        self.n_pos = int(vi.cu_positions[-1])
+        self.cu_p = to_device(vi.cu_positions, device)
+        self.draft = to_device(vi.draft, device)
+        self.logits = to_device(vi.logits, device) if vi.logits is not None else None
+        self.argmax = torch.empty(self.R, dtype=torch.int32, device=device)
+        self.conf = torch.empty(self.R, dtype=torch.float32, device=device)
+        self.accept_row = torch.empty(self.R, dtype=torch.uint8, device=device)
+        self.accept_pos = torch.empty(self.n_pos, dtype=torch.uint8, device=device)
+
+    def qkv(self, stream=None):
+        s = self.step
+        fc.fc_qkv_rope_cache_write(s.hidden, s.positions, s.cu_q, s.B, s.T_q, s.w_qkv, s.d, s.H,
+                                   s.D, s.cfg.rope_base, None, None, s.block_table,
+                                   s.inp.max_pages, s.cfg.page_size, s.q_out, s.slot_mapping,
+                                   s.dtype, stream)
+
+    def attention(self, stream=None):
+        self.step.attention(stream, importance=False)
+
+    def verify(self, stream=None):
+        fc.fv_verify_accept(self.logits, self.V, self.cu_p, self.step.B, self.R, self.draft,
+                            self.tau, self.argmax, self.conf, self.accept_row, self.accept_pos,
+                            stream)
+
+    def run(self, stream=None):
+        self.qkv(stream)
+        self.attention(stream)
+        self.verify(stream)
+
+    def fetch(self):
+        out = dict(argmax=to_host(self.argmax), conf=to_host(self.conf),
+                   accept_row=to_host(self.accept_row), accept_pos=to_host(self.accept_pos),
+                   q_out=to_host(self.step.q_out), attn_out=to_host(self.step.attn_out))
+        return out

@@ -33,9 +33,13 @@ def rng_for(seed: int, *tags: int) -> np.random.Generator:
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round to nearest even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return b.astype(np.uint16)
+    b = x.view(np.uint32)
+    nan = np.isnan(x)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    r = r.astype(np.uint16)
+    if nan.any():
+        r[nan] = (b[nan] >> np.uint32(16)).astype(np.uint16) | np.uint16(0x40)
+    return r
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -313,3 +317,19 @@ def draw_logits(vi: VerifyInputs, row_block: int = 256) -> np.ndarray:
                 x[r - r0, vi.target[p]] = np.float32(planted_logit(c[r], V, cfg.logit_std))
         out[r0:r1] = to_bf16_bits(x)
     return out
+
+
+def sequence_inputs(inp: StepInputs, b: int) -> dict:
+    """Sequence b of a batch on its own: its query rows and only its own cache
+    pages (page ids renumbered 0..n-1, `pages` maps them back)."""
+    cfg = inp.cfg
+    q0, q1 = int(inp.cu_seqlens_q[b]), int(inp.cu_seqlens_q[b + 1])
+    L = int(inp.cache_len[b])
+    n_pages = (L + cfg.page_size - 1) // cfg.page_size
+    pages = inp.block_table[b, :n_pages]
+    return dict(hidden=inp.hidden[q0:q1], positions=inp.positions[q0:q1],
+                cu_q=np.array([0, q1 - q0], np.int32), cu_k=np.array([0, L], np.int32),
+                k_cache=inp.k_cache[pages], v_cache=inp.v_cache[pages],
+                block_table=np.arange(n_pages, dtype=np.int32)[None, :], pages=pages,
+                cand=inp.cand_mask[int(inp.cu_seqlens_k[b]): int(inp.cu_seqlens_k[b + 1])],
+                q0=q0, q1=q1, L=L)

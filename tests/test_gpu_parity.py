@@ -1,0 +1,282 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same
+seeded inputs. Run on an MI355X: pytest -m gpu."""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from kv_cache_attention_step_amd import configs as CF
+from kv_cache_attention_step_amd import workload as W
+from oracle import flashcache_oracle as O
+from tests import parity_util as PU
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    from kv_cache_attention_step_amd import flashcache as fc
+    fc.load()  # fail loudly when the library is missing
+    return torch
+
+
+def run_gpu_step(inp, torch):
+    from kv_cache_attention_step_amd.runner import StepBuffers
+    bufs = StepBuffers(inp)
+    bufs.run()
+    torch.cuda.synchronize()
+    return bufs.fetch()
+
+
+def check_cache(got_cache, in_cache, ref_rows, slots, page_size, H, dtype, what):
+    """Written slots against the oracle's unrounded rows, every other slot bit-exact."""
+    pages = slots // page_size
+    offs = slots % page_size
+    written = got_cache[pages, :, offs, :]                        # [T, H, D]
+    PU.assert_close(PU.as_f64(written, dtype), ref_rows, dtype, what + " written rows")
+    mask = np.ones(got_cache.shape[0] * page_size, bool)
+    mask[slots] = False
+    g = got_cache.transpose(0, 2, 1, 3).reshape(-1, H, got_cache.shape[-1])
+    i = in_cache.transpose(0, 2, 1, 3).reshape(-1, H, in_cache.shape[-1])
+    gb = g[mask].view(np.uint32 if g.dtype == np.float32 else np.uint16)
+    ib = i[mask].view(np.uint32 if i.dtype == np.float32 else np.uint16)
+    assert np.array_equal(gb, ib), f"{what}: untouched slots changed"
+
+
+def full_parity(inp, got):
+    cfg = inp.cfg
+    r = O.flash_cache_step(inp.hidden, inp.positions, inp.cu_seqlens_q, inp.cu_seqlens_k,
+                           inp.w_qkv, cfg.n_heads, cfg.head_dim, cfg.rope_base, inp.k_cache,
+                           inp.v_cache, inp.block_table, cfg.page_size, inp.cand_mask, cfg.track,
+                           cfg.dtype)
+    dt = cfg.dtype
+    assert np.array_equal(got["slot_mapping"].astype(np.int64), r["slot_mapping"]), "slot mapping"
+    PU.assert_close(PU.as_f64(got["q_out"], dt), r["q"], dt, "q_out")
+    check_cache(got["k_cache"], inp.k_cache, r["k"], r["slot_mapping"], cfg.page_size,
+                cfg.n_heads, dt, "k_cache")
+    check_cache(got["v_cache"], inp.v_cache, r["v"], r["slot_mapping"], cfg.page_size,
+                cfg.n_heads, dt, "v_cache")
+    PU.assert_close(PU.as_f64(got["attn_out"], dt), r["out"], dt, "attention out")
+    PU.assert_importance_close(got["importance"], r["importance"])
+    score = r["importance"].sum(0)
+    n_near = 0
+    for b in range(inp.B):
+        k0, k1 = int(inp.cu_seqlens_k[b]), int(inp.cu_seqlens_k[b + 1])
+        n_near += PU.assert_topk_matches(got["topk_pos"][b], int(got["topk_count"][b]),
+                                         score[k0:k1], inp.cand_mask[k0:k1], cfg.track,
+                                         f"topk seq {b}")
+    return r, n_near
+
+
+def test_c0_tiny_fp32_step(torch_cuda):
+    _say("case C0 tiny fp32 step")
+    inp = W.make_step_inputs(CF.C0)
+    got = run_gpu_step(inp, torch_cuda)
+    full_parity(inp, got)
+
+
+SMALL_BF16 = dataclasses.replace(CF.C2, name="C2-small", seed=21, batch=3, d_model=512, n_heads=4,
+                                 prompt=(40, 300), gen_len=160, window=48, track=40)
+
+
+def test_small_bf16_varlen_step_with_nan_tails(torch_cuda):
+    """Several sequences, ragged key tiles and pages; slots past each sequence end
+    hold NaN and must never be read."""
+    _say("case C2-small bf16 varlen, NaN tails")
+    inp = W.make_step_inputs(SMALL_BF16, tail_nan=True)
+    got = run_gpu_step(inp, torch_cuda)
+    full_parity(inp, got)
+
+
+def test_bf16_query_longer_than_one_row_tile(torch_cuda):
+    """Q_b > 128 rows: the importance path loops over row tiles in one workgroup."""
+    cfg = dataclasses.replace(SMALL_BF16, name="C2-rows", seed=22, batch=2, prompt=(100, 180),
+                              gen_len=300, window=100, track=90)
+    _say("case C2-rows bf16 Q_b=190")
+    inp = W.make_step_inputs(cfg)
+    got = run_gpu_step(inp, torch_cuda)
+    full_parity(inp, got)
+
+
+def test_c1_single_layer_step(torch_cuda):
+    _say("case C1 full step")
+    inp = W.make_step_inputs(CF.C1)
+    got = run_gpu_step(inp, torch_cuda)
+    full_parity(inp, got)
+
+
+def test_c2_full_size_sampled(torch_cuda):
+    """Full C2 shapes in the launch configuration the benchmark times; the oracle
+    recomputes two whole sequences (all heads) and invariants cover the rest."""
+    _say("case C2 full size, sampled sequences")
+    cfg = CF.C2
+    inp = W.make_step_inputs(cfg)
+    got = run_gpu_step(inp, torch_cuda)
+    dt = cfg.dtype
+    H, D = cfg.n_heads, cfg.head_dim
+    # invariants over every sequence and head: column sums add up to Q_b per head
+    imp = got["importance"].astype(np.float64)
+    assert np.all(np.isfinite(imp)) and np.all(imp >= 0)
+    for b in range(inp.B):
+        k0, k1 = int(inp.cu_seqlens_k[b]), int(inp.cu_seqlens_k[b + 1])
+        qb = int(inp.cu_seqlens_q[b + 1] - inp.cu_seqlens_q[b])
+        np.testing.assert_allclose(imp[:, k0:k1].sum(1), qb, rtol=2e-4)
+        assert int(got["topk_count"][b]) == cfg.track
+    assert np.all(np.isfinite(PU.as_f64(got["attn_out"], dt)))
+    # two sampled sequences in full
+    for b in (0, inp.B - 1):
+        s = PU.compact_sequence(inp, b)
+        r = O.flash_cache_step(s["hidden"], s["positions"], s["cu_q"], s["cu_k"], inp.w_qkv, H, D,
+                               cfg.rope_base, s["k_cache"], s["v_cache"], s["block_table"],
+                               cfg.page_size, s["cand"], cfg.track, dt)
+        q0, q1 = s["q0"], s["q1"]
+        # slots in the real page numbering
+        slot_real = s["pages"][r["slot_mapping"] // cfg.page_size] * cfg.page_size + \
+            r["slot_mapping"] % cfg.page_size
+        assert np.array_equal(got["slot_mapping"][q0:q1].astype(np.int64), slot_real)
+        PU.assert_close(PU.as_f64(got["q_out"][q0:q1], dt), r["q"], dt, f"q_out seq {b}")
+        pg, off = slot_real // cfg.page_size, slot_real % cfg.page_size
+        PU.assert_close(PU.as_f64(got["k_cache"][pg, :, off, :], dt), r["k"], dt, f"k seq {b}")
+        PU.assert_close(PU.as_f64(got["v_cache"][pg, :, off, :], dt), r["v"], dt, f"v seq {b}")
+        PU.assert_close(PU.as_f64(got["attn_out"][q0:q1], dt), r["out"], dt, f"attn seq {b}")
+        k0, k1 = int(inp.cu_seqlens_k[b]), int(inp.cu_seqlens_k[b + 1])
+        PU.assert_importance_close(got["importance"][:, k0:k1], r["importance"], f"imp seq {b}")
+        PU.assert_topk_matches(got["topk_pos"][b], int(got["topk_count"][b]),
+                               r["importance"].sum(0), s["cand"], cfg.track, f"topk seq {b}")
+
+
+def test_c2_deterministic(torch_cuda):
+    """Same inputs twice -> bit-identical outputs (no float atomics anywhere)."""
+    _say("case C2 determinism")
+    torch = torch_cuda
+    from kv_cache_attention_step_amd.runner import StepBuffers
+    inp = W.make_step_inputs(CF.C2)
+    bufs = StepBuffers(inp)
+    outs = []
+    for _ in range(2):
+        bufs.run()
+        torch.cuda.synchronize()
+        f = bufs.fetch()
+        outs.append({k: f[k] for k in ("q_out", "attn_out", "importance", "topk_pos",
+                                        "topk_score", "slot_mapping")})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
+
+
+def test_topk_kernel_planted_ties(torch_cuda):
+    """Importance built by the test with many exact ties: the kernel's selection
+    must equal the oracle's, both deciding on the same fp32 head-sum."""
+    torch = torch_cuda
+    from kv_cache_attention_step_amd import flashcache as fc
+    _say("case topk planted ties")
+    rng = np.random.default_rng(5)
+    H = 8
+    lens = np.array([1, 7, 64, 300, 1537, 4096, 0, 33])
+    B = len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T_k = int(cu[-1])
+    imp = (rng.integers(0, 6, size=(H, T_k)) / 8.0).astype(np.float32)   # exact, many ties
+    cand = (rng.random(T_k) < 0.7).astype(np.uint8)
+    for k in (1, 5, 64, 500):
+        d_imp = torch.from_numpy(imp).cuda()
+        d_cu = torch.from_numpy(cu).cuda()
+        d_cand = torch.from_numpy(cand).cuda()
+        pos = torch.full((B, k), 77, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+        sc = torch.zeros((B, k), dtype=torch.float32, device="cuda")
+        fc.fc_importance_topk(d_imp, d_cu, B, T_k, H, d_cand, k, pos, cnt, sc)
+        torch.cuda.synchronize()
+        opos, ocnt, osc, _ = O.importance_topk(imp.astype(np.float64), cu, cand, k,
+                                                score_float32=True)
+        assert np.array_equal(cnt.cpu().numpy(), ocnt), f"k={k} counts"
+        assert np.array_equal(pos.cpu().numpy(), opos), f"k={k} positions"
+        gsc = sc.cpu().numpy()
+        assert np.array_equal(np.nan_to_num(gsc, nan=-1), np.nan_to_num(osc.astype(np.float32),
+                                                                        nan=-1)), f"k={k} scores"
+
+
+def test_linear_residual_bf16(torch_cuda):
+    torch = torch_cuda
+    from kv_cache_attention_step_amd import flashcache as fc
+    from kv_cache_attention_step_amd.runner import to_device, to_host
+    _say("case linear residual bf16 300x512x1024")
+    rng = W.rng_for(9, 1)
+    M, N, K = 300, 512, 1024
+    x = W.to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    w = W.to_bf16_bits((rng.standard_normal((N, K), dtype=np.float32) * 0.02).astype(np.float32))
+    h = W.to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
+    dx, dw, dh = to_device(x), to_device(w), to_device(h)
+    fc.fc_linear_residual(dx, dw, dh, M, N, K, fc.FC_DTYPE_BF16)
+    torch.cuda.synchronize()
+    ref = O.linear_residual(x, w, h, "bf16")
+    PU.assert_close(O.bf16_to_f64(to_host(dh)), ref, "bf16", "h + x W^T")
+
+
+def test_degenerate_sequences(torch_cuda):
+    """A sequence with no query rows, one with a single cached key, and a tracking
+    budget larger than the candidate count."""
+    torch = torch_cuda
+    from kv_cache_attention_step_amd.runner import StepBuffers
+    _say("case degenerate sequences")
+    cfg = dataclasses.replace(SMALL_BF16, name="degenerate", seed=23, batch=3, prompt=(1, 1),
+                              gen_len=0, window=0, track=0)
+    H, D, ps = cfg.n_heads, cfg.head_dim, cfg.page_size
+    rng = W.rng_for(23, 9)
+    L = np.array([1, 40, 17], np.int32)
+    Q = np.array([1, 0, 5], np.int32)
+    table, num_pages = W.draw_paging(cfg, L.astype(np.int64), rng)
+    k_cache, v_cache = W.draw_cache(cfg, num_pages, rng)
+    pos = np.concatenate([[0], rng.choice(17, 5, replace=False)]).astype(np.int32)
+    cu_q = np.concatenate([[0], np.cumsum(Q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    cand = (rng.random(int(cu_k[-1])) < 0.5).astype(np.uint8)
+    inp = W.StepInputs(cfg=dataclasses.replace(cfg, track=50), dtype="bf16",
+                       hidden=W.to_bf16_bits(rng.standard_normal((6, cfg.d_model),
+                                                                 dtype=np.float32)),
+                       positions=pos, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                       w_qkv=W.to_bf16_bits((rng.standard_normal((3 * cfg.d_model, cfg.d_model),
+                                                                 dtype=np.float32) * 0.02)),
+                       k_cache=k_cache, v_cache=v_cache, block_table=table, cand_mask=cand,
+                       prompt_len=L, cache_len=L, window_start=L, tracked=np.zeros((3, 0), np.int32))
+    got = run_gpu_step(inp, torch)
+    r, _ = full_parity(inp, got)
+    # no query rows -> zero importance for that sequence
+    assert np.all(got["importance"][:, cu_k[1]:cu_k[2]] == 0)
+
+
+def test_verify_small_vocab(torch_cuda):
+    torch = torch_cuda
+    from kv_cache_attention_step_amd.runner import VerifyBuffers
+    _say("case verify small vocab")
+    cfg = dataclasses.replace(CF.C4, name="C4-small", seed=41, batch=5, vocab=1000,
+                              verify_len=(3, 20), d_model=256, n_heads=2)
+    vi = W.make_verify_inputs(cfg)
+    vb = VerifyBuffers(vi)
+    vb.verify()
+    torch.cuda.synchronize()
+    got = vb.fetch()
+    am, conf, acc, acc_pos = O.verify_accept(vi.logits, vi.cu_positions, vi.draft, cfg.tau)
+    assert np.array_equal(got["argmax"], am)
+    np.testing.assert_allclose(got["conf"], conf, rtol=2e-6)
+    # rows whose exact confidence sits within 1e-5 of tau may go either way in fp32
+    near = np.abs(conf - cfg.tau) <= 1e-5
+    assert np.array_equal(got["accept_row"][~near], acc[~near])
+    rows = got["accept_row"]
+    for b in range(cfg.batch):
+        p0, p1 = int(vi.cu_positions[b]), int(vi.cu_positions[b + 1])
+        n = p1 - p0
+        # accept_pos is the AND of the position's two view rows
+        exp = rows[2 * p0: 2 * p0 + n] & rows[2 * p0 + n: 2 * p0 + 2 * n]
+        assert np.array_equal(got["accept_pos"][p0:p1], exp)
+        near_pos = near[2 * p0: 2 * p0 + n] | near[2 * p0 + n: 2 * p0 + 2 * n]
+        assert np.array_equal(got["accept_pos"][p0:p1][~near_pos], acc_pos[p0:p1][~near_pos])
+    assert acc.sum() > 0 and (acc == 0).sum() > 0   # both outcomes exercised
