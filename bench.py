@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib", action="store_true",
+                    help="run one 256 MiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--cpu-seqs", type=int, default=32,
                     help="sequences of the batch the CPU oracle baseline runs")
     return ap.parse_args()
@@ -125,6 +127,13 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    if args.calib:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()

@@ -141,8 +141,10 @@ size_t fc_attention_workspace_size(int32_t B, int32_t T_q, int32_t T_k, int32_t 
  * max_seqlen_q                max Q_b (sizes the grid; rows beyond Q_b idle)
  * out           [T_q, H, D]  dtype
  * importance    [H, T_k] fp32 or NULL
- * workspace     device memory of fc_attention_workspace_size() bytes, or NULL
- *               when that size is 0
+ * workspace     device memory of at least fc_attention_workspace_size() bytes
+ *               (scratch for the longest-first sequence order; contents need no
+ *               initialisation and are overwritten; calls that overlap on one
+ *               workspace race)
  * A sequence with L_b = 0 gets out = 0. Supported: bf16 with D = 128; f32 with
  * D in {64, 128}.
  */

@@ -37,7 +37,7 @@
 namespace {
 
 constexpr int AD = 128;                 // head dim
-constexpr int AKT = 64;                 // keys per tile
+constexpr int AKT = 64;                 // keys per tile (4 groups of 16, one per wave)
 constexpr int AROWS = 128;              // query rows per workgroup pass
 constexpr int K_STRIDE = AD * 2 + 16;   // bytes per key row of the K tile
 constexpr int V_STRIDE = AKT * 2 + 8;   // bytes per dim row of the V^T tile
@@ -55,68 +55,107 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* cu_q;
   const int32_t* cu_k;
+  const int32_t* order;   // sequences, longest cache first (NULL = natural order)
   uint16_t* out;
   float* imp;
   int maxp, log2ps, B, H, T_k, n_rt, accumulate;
   float scale_log2;  // softmax_scale * log2(e)
 };
 
+FC_DEVICE float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+FC_DEVICE uint32_t pack2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 // ---- tile loads ----------------------------------------------------------
-// K: thread t loads 16-byte chunk (t & 15) of keys (t >> 4) + 16 j, j < 4.
-FC_DEVICE void load_k(const AttnArgs& a, const int32_t* bt, int h, int tile, int L,
-                      u32x4_t (&r)[4]) {
-  const int t = threadIdx.x;
+// Wave g of the workgroup loads key group g (16 keys) of the tile, K and V.
+// Loads past the last tile are harmless (zero-length descriptor or key check)
+// and are issued unconditionally so the compiler's wait counts stay exact.
+// K: lane l loads 16-byte chunk (l & 15) of keys (l >> 4) + 4 i.
+// V: lane l loads dims 8 (l >> 2) .. +7 of keys 4 (l & 3) .. +3 (transposed on store).
+struct TileRegs {
+  u32x4_t k[4];
+  u32x4_t v[4];
+};
+
+template <bool PS_GE16, bool WANT_V>
+FC_DEVICE void load_group(const AttnArgs& a, const int32_t* __restrict__ bt, int h, int tile, int L,
+                          int g, int lane, TileRegs& r) {
+  const int key0 = tile * AKT + g * 16;
   const int psm = (1 << a.log2ps) - 1;
+  const size_t head_stride = (size_t)(psm + 1) * AD;          // elements of one (page, head)
+  const size_t page_stride = head_stride * a.H;
+  if (PS_GE16) {
+    // the 16 keys share one page: one descriptor per wave, clipped at the
+    // sequence end so that keys >= L read as 0
+    const int nvalid = min(16, L - key0);
+    int page = 0;
+    if (nvalid > 0) page = bt[key0 >> a.log2ps];
+    const size_t base = (size_t)page * page_stride + (size_t)h * head_stride + (size_t)(key0 & psm) * AD;
+    const uint32_t bytes = nvalid > 0 ? (uint32_t)nvalid * AD * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc + base, bytes);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int key = tile * AKT + (t >> 4) + 16 * j;
-    if (key < L) {
-      const int page = bt[key >> a.log2ps];
-      const size_t off = (((size_t)page * a.H + h) * (psm + 1) + (key & psm)) * AD + (t & 15) * 8;
-      r[j] = *(const u32x4_t*)(a.kc + off);
-    } else {
-      r[j] = u32x4_t{0, 0, 0, 0};
+    for (int i = 0; i < 4; ++i)
+      r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((lane >> 4) + 4 * i) * (AD * 2) + (lane & 15) * 16, 0, 0);
+    if (WANT_V) {
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vc + base, bytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (4 * (lane & 3) + i) * (AD * 2) + (lane >> 2) * 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = key0 + (lane >> 4) + 4 * i;
+      if (key < L) {
+        const size_t off = (size_t)bt[key >> a.log2ps] * page_stride + (size_t)h * head_stride +
+                           (size_t)(key & psm) * AD + (lane & 15) * 8;
+        r.k[i] = *(const u32x4_t*)(a.kc + off);
+      } else {
+        r.k[i] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+    if (WANT_V) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = key0 + 4 * (lane & 3) + i;
+        if (key < L) {
+          const size_t off = (size_t)bt[key >> a.log2ps] * page_stride + (size_t)h * head_stride +
+                             (size_t)(key & psm) * AD + (lane >> 2) * 8;
+          r.v[i] = *(const u32x4_t*)(a.vc + off);
+        } else {
+          r.v[i] = u32x4_t{0, 0, 0, 0};
+        }
+      }
     }
   }
 }
-FC_DEVICE void store_k(char* ks, const u32x4_t (&r)[4]) {
-  const int t = threadIdx.x;
+
+template <bool WANT_V>
+FC_DEVICE void store_group(char* stage, int g, int lane, const TileRegs& r) {
+  char* ks = stage;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) *(u32x4_t*)(ks + ((t >> 4) + 16 * j) * K_STRIDE + (t & 15) * 16) = r[j];
-}
-// V: thread t loads keys 4 (t & 15) .. +3, dims 8 (t >> 4) .. +7, and writes them
-// transposed (4 keys of one dim = 8 bytes) into V^T.
-FC_DEVICE void load_v(const AttnArgs& a, const int32_t* bt, int h, int tile, int L,
-                      u32x4_t (&r)[4]) {
-  const int t = threadIdx.x;
-  const int psm = (1 << a.log2ps) - 1;
+  for (int i = 0; i < 4; ++i)
+    *(u32x4_t*)(ks + (g * 16 + (lane >> 4) + 4 * i) * K_STRIDE + (lane & 15) * 16) = r.k[i];
+  if (WANT_V) {
+    char* vs = stage + K_TILE;
+    const int key0 = g * 16 + 4 * (lane & 3);
+    const int d0 = 8 * (lane >> 2);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int key = tile * AKT + 4 * (t & 15) + j;
-    if (key < L) {
-      const int page = bt[key >> a.log2ps];
-      const size_t off = (((size_t)page * a.H + h) * (psm + 1) + (key & psm)) * AD + (t >> 4) * 8;
-      r[j] = *(const u32x4_t*)(a.vc + off);
-    } else {
-      r[j] = u32x4_t{0, 0, 0, 0};
+    for (int p = 0; p < 4; ++p) {
+      // r.v[j][p] holds dim d0 + 2p (low half) and d0 + 2p + 1 (high half) of key j
+      const uint32_t w0 = r.v[0][p], w1 = r.v[1][p], w2 = r.v[2][p], w3 = r.v[3][p];
+      u32x2_t lo, hi;
+      lo[0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+      hi[0] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+      hi[1] = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+      *(u32x2_t*)(vs + (d0 + 2 * p) * V_STRIDE + key0 * 2) = lo;
+      *(u32x2_t*)(vs + (d0 + 2 * p + 1) * V_STRIDE + key0 * 2) = hi;
     }
-  }
-}
-FC_DEVICE void store_v(char* vs, const u32x4_t (&r)[4]) {
-  const int t = threadIdx.x;
-  const int key0 = 4 * (t & 15);
-  const int d0 = 8 * (t >> 4);
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    // r[j][p] holds dims (d0 + 2p) in its low half and (d0 + 2p + 1) in its high half
-    const uint32_t w0 = r[0][p], w1 = r[1][p], w2 = r[2][p], w3 = r[3][p];
-    u32x2_t lo, hi;
-    lo[0] = (w0 & 0xFFFFu) | (w1 << 16);
-    lo[1] = (w2 & 0xFFFFu) | (w3 << 16);
-    hi[0] = (w0 >> 16) | (w1 & 0xFFFF0000u);
-    hi[1] = (w2 >> 16) | (w3 & 0xFFFF0000u);
-    *(u32x2_t*)(vs + (d0 + 2 * p) * V_STRIDE + key0 * 2) = lo;
-    *(u32x2_t*)(vs + (d0 + 2 * p + 1) * V_STRIDE + key0 * 2) = hi;
   }
 }
 
@@ -134,12 +173,13 @@ FC_DEVICE f32x16_t s_block(const char* ks, int kb, const bf16x8_t (&qf)[8], int 
 FC_DEVICE int s_key(int kb, int i, int lane) { return kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
 
 // O^T += V^T P^T for the 16 keys of chunk c of block kb; p holds block kb's
-// probabilities (16 registers).
+// probabilities (16 registers). The B operand's k index 8*(l/32) + j is key
+// 16c + 8*(j/4) + 4*(l/32) + j%4 of the block; the V^T reads use the same map.
 FC_DEVICE void pv_chunk(const char* vs, int kb, int c, const f32x16_t& p, f32x16_t (&o)[4],
                         int lane) {
   u32x4_t pb;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
+  for (int w = 0; w < 4; ++w) pb[w] = pack2(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
   const bf16x8_t bop = as_bf16x8(pb);
   const int kbase = kb * 32 + c * 16 + (lane >> 5) * 4;
 #pragma unroll
@@ -175,56 +215,92 @@ FC_DEVICE void store_o(const AttnArgs& a, int q0, int row, int Q, int h, const f
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2_t w;
-      w[0] = pack_bf16x2(o[db][4 * g] * scale, o[db][4 * g + 1] * scale);
-      w[1] = pack_bf16x2(o[db][4 * g + 2] * scale, o[db][4 * g + 3] * scale);
+      w[0] = pack2(o[db][4 * g] * scale, o[db][4 * g + 1] * scale);
+      w[1] = pack2(o[db][4 * g + 2] * scale, o[db][4 * g + 3] * scale);
       *(u32x2_t*)(dst + db * 32 + g * 8) = w;
     }
 }
 
-// Sum over the 32 lanes of each half-wave of the 16 values a lane holds;
-// afterwards lanes l and l^1 both hold the sum of value index (l >> 1) & 15.
-FC_DEVICE float transpose_reduce16(f32x16_t& v, int lane) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) {
-    const int lm = m * 2;  // lane bit that decides which half of the values is kept
-    const bool up = (lane & lm) != 0;
-#pragma unroll
-    for (int j = 0; j < m; ++j) {
-      const float send = up ? v[j] : v[j + m];
-      const float keep = up ? v[j + m] : v[j];
-      v[j] = keep + __shfl_xor(send, lm);
-    }
-  }
-  return v[0] + __shfl_xor(v[0], 1);
+// DPP lane moves within rows of 16 lanes
+FC_DEVICE float dpp_mirror(float x) {      // lane i <- lane 15 - i
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+}
+FC_DEVICE float dpp_half_mirror(float x) { // lane i <- lane 7 - i (within 8)
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+}
+FC_DEVICE float dpp_xor2(float x) {        // quad_perm [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+FC_DEVICE float dpp_xor1(float x) {        // quad_perm [1,0,3,2]
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
+// Sum over the 32 lanes of each half-wave of the 16 values a lane holds.
+// Each step halves the values a lane keeps; which half is decided by one lane
+// bit (4, 3, 2, 1), and the partner lane (differing in that bit and possibly in
+// lower ones: rows swap, mirror, half-mirror, xor 2) keeps the other half. The
+// partner masks 16, 15, 7, 2, 1 are independent, so every lane of the half is
+// summed exactly once. Afterwards lanes l and l^1 both hold the sum of value
+// index (l >> 1) & 15.
+FC_DEVICE float transpose_reduce16(f32x16_t& v, int lane) {
+  // bit 4: exchange with the other 16-lane row of the half
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j + 8]),
+                                                     false, false);
+    v[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float send = b3 ? v[j] : v[j + 4];
+    const float keep = b3 ? v[j + 4] : v[j];
+    v[j] = keep + dpp_mirror(send);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float send = b2 ? v[j] : v[j + 2];
+    const float keep = b2 ? v[j + 2] : v[j];
+    v[j] = keep + dpp_half_mirror(send);
+  }
+  {
+    const float send = b1 ? v[0] : v[1];
+    const float keep = b1 ? v[1] : v[0];
+    v[0] = keep + dpp_xor2(send);
+  }
+  return v[0] + dpp_xor1(v[0]);
+}
+
+// value index -> key of the tile after transpose_reduce16 of block kb
+FC_DEVICE int reduced_key(int kb, int lane) { return s_key(kb, (lane >> 1) & 15, lane); }
+
 // ---- kernels -------------------------------------------------------------------
-template <bool WITH_IMP>
+template <bool WITH_IMP, bool PS_GE16>
 __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[A_LDS];
   float* red = (float*)(lds + 2 * A_STAGE);
 
   int item = blockIdx.x;
   int rt_begin, rt_end;
-  int b, h;
   if (WITH_IMP) {
-    b = item / a.H;
-    h = item % a.H;
     rt_begin = 0;
     rt_end = a.n_rt;
   } else {
-    const int rt = item % a.n_rt;
+    rt_begin = item % a.n_rt;
+    rt_end = rt_begin + 1;
     item /= a.n_rt;
-    b = item / a.H;
-    h = item % a.H;
-    rt_begin = rt;
-    rt_end = rt + 1;
   }
+  const int sr = item / a.H;
+  const int h = item % a.H;
+  const int b = a.order ? a.order[sr] : sr;
   const int q0 = a.cu_q[b], Q = a.cu_q[b + 1] - q0;
   const int k0 = a.cu_k[b], L = a.cu_k[b + 1] - k0;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int32_t* bt = a.block_table + (size_t)b * a.maxp;
   const int n_tiles = (L + AKT - 1) / AKT;
+  const bool ragged = (L & (AKT - 1)) != 0;   // last tile partly past the end
+  const float c = a.scale_log2;
 
   if (WITH_IMP && Q == 0 && !a.accumulate) {  // no query rows: column sums are 0
     for (int key = t; key < L; key += blockDim.x) a.imp[(size_t)h * a.T_k + k0 + key] = 0.f;
@@ -242,59 +318,56 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
     bf16x8_t qf[8];
     load_q(a, q0, row, Q, h, qf);
     f32x16_t o[4] = {};
-    u32x4_t rk[4], rv[4];
+    TileRegs tr;
 
     if (WITH_IMP) {
-      // ---------------- pass 1: row max and normaliser ----------------
+      // ---------------- pass 1: row max and normaliser (K only) ----------------
       float m = -INFINITY, l = 0.f;
-      load_k(a, bt, h, 0, L, rk);
-      store_k(lds, rk);
+      load_group<PS_GE16, false>(a, bt, h, 0, L, wave, lane, tr);
+      store_group<false>(lds, wave, lane, tr);
       __syncthreads();
       for (int tile = 0; tile < n_tiles; ++tile) {
         const bool more = tile + 1 < n_tiles;
-        if (more) load_k(a, bt, h, tile + 1, L, rk);
+        load_group<PS_GE16, false>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
-        float x[32];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const f32x16_t s = s_block(ks, kb, qf, lane);
+        f32x16_t s0 = s_block(ks, 0, qf, lane);
+        f32x16_t s1 = s_block(ks, 1, qf, lane);
+        if (ragged && !more) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = tile * AKT + s_key(kb, i, lane);
-            const float v = key < L ? s[i] * a.scale_log2 : -INFINITY;
-            x[kb * 16 + i] = v;
-            tmax = fmaxf(tmax, v);
+            if (tile * AKT + s_key(0, i, lane) >= L) s0[i] = -INFINITY;
+            if (tile * AKT + s_key(1, i, lane) >= L) s1[i] = -INFINITY;
           }
         }
-        const float mn = fmaxf(m, tmax);
-        const float mref = mn == -INFINITY ? 0.f : mn;  // this lane has seen no key yet
+        float tmax = s0[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s0[i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
+        const float mn = fmaxf(m, tmax * c);
+        const float mref = mn == -INFINITY ? 0.f : mn;   // this lane has seen no key yet
         float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) sum += exp2f(x[j] - mref);
-        l = (m == -INFINITY ? 0.f : l * exp2f(m - mn)) + sum;
+        for (int i = 0; i < 16; ++i) sum += fexp2(fmaf(s0[i], c, -mref)) + fexp2(fmaf(s1[i], c, -mref));
+        l = (m == -INFINITY ? 0.f : l * fexp2(m - mn)) + sum;
         m = mn;
-        if (more) store_k(lds + ((tile + 1) & 1) * A_STAGE, rk);
+        store_group<false>(lds + ((tile + 1) & 1) * A_STAGE, wave, lane, tr);
         __syncthreads();
       }
       const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
       const float mf = fmaxf(m, mo);
-      const float lf = (m == -INFINITY ? 0.f : l * exp2f(m - mf)) +
-                       (mo == -INFINITY ? 0.f : lo * exp2f(mo - mf));
-      const float inv_l = row_ok ? 1.f / lf : 0.f;
+      const float lf = (m == -INFINITY ? 0.f : l * fexp2(m - mf)) +
+                       (mo == -INFINITY ? 0.f : lo * fexp2(mo - mf));
+      // P = exp2(s c - mf) / lf = exp2(s c - (mf + log2 lf)); rows past Q get P = 0
+      const float mf2 = row_ok ? mf + __log2f(lf) : INFINITY;
 
       // ---------------- pass 2: P, O += P V, importance ----------------
-      load_k(a, bt, h, 0, L, rk);
-      load_v(a, bt, h, 0, L, rv);
-      store_k(lds, rk);
-      store_v(lds + K_TILE, rv);
+      load_group<PS_GE16, true>(a, bt, h, 0, L, wave, lane, tr);
+      store_group<true>(lds, wave, lane, tr);
       __syncthreads();
       for (int tile = 0; tile < n_tiles; ++tile) {
         const bool more = tile + 1 < n_tiles;
-        if (more) {
-          load_k(a, bt, h, tile + 1, L, rk);
-          load_v(a, bt, h, tile + 1, L, rv);
-        }
+        load_group<PS_GE16, true>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
         const char* vs = ks + K_TILE;
         float* rb = red + (tile & 1) * 4 * AKT;
@@ -302,24 +375,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb) {
           f32x16_t s = s_block(ks, kb, qf, lane);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = tile * AKT + s_key(kb, i, lane);
-            s[i] = key < L ? exp2f(s[i] * a.scale_log2 - mf) * inv_l : 0.f;
+          for (int i = 0; i < 16; ++i) s[i] = fexp2(fmaf(s[i], c, -mf2));
+          if (ragged && !more) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (tile * AKT + s_key(kb, i, lane) >= L) s[i] = 0.f;
           }
           pv_chunk(vs, kb, 0, s, o, lane);
           pv_chunk(vs, kb, 1, s, o, lane);
-          // column sums over this wave's 32 query rows: lanes l and l^1 end with
-          // the sum of register index (l >> 1) & 15
+          // column sums over this wave's 32 query rows
           const float colsum = transpose_reduce16(s, lane);
-          if ((lane & 1) == 0) {
-            const int r = (lane >> 1) & 15;
-            rb[wave * AKT + s_key(kb, r, lane)] = colsum;
-          }
+          if ((lane & 1) == 0) rb[wave * AKT + reduced_key(kb, lane)] = colsum;
         }
-        if (more) {
-          store_k(lds + ((tile + 1) & 1) * A_STAGE, rk);
-          store_v(lds + ((tile + 1) & 1) * A_STAGE + K_TILE, rv);
-        }
+        store_group<true>(lds + ((tile + 1) & 1) * A_STAGE, wave, lane, tr);
         __syncthreads();
         if (t < AKT) {
           const int key = tile * AKT + t;
@@ -335,65 +403,71 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
     } else {
       // ---------------- single pass, online softmax ----------------
       float m = -INFINITY, l = 0.f;
-      load_k(a, bt, h, 0, L, rk);
-      load_v(a, bt, h, 0, L, rv);
-      store_k(lds, rk);
-      store_v(lds + K_TILE, rv);
+      load_group<PS_GE16, true>(a, bt, h, 0, L, wave, lane, tr);
+      store_group<true>(lds, wave, lane, tr);
       __syncthreads();
       for (int tile = 0; tile < n_tiles; ++tile) {
         const bool more = tile + 1 < n_tiles;
-        if (more) {
-          load_k(a, bt, h, tile + 1, L, rk);
-          load_v(a, bt, h, tile + 1, L, rv);
-        }
+        load_group<PS_GE16, true>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
         const char* vs = ks + K_TILE;
-        f32x16_t s[2];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = s_block(ks, kb, qf, lane);
+        f32x16_t s0 = s_block(ks, 0, qf, lane);
+        f32x16_t s1 = s_block(ks, 1, qf, lane);
+        if (ragged && !more) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = tile * AKT + s_key(kb, i, lane);
-            const float v = key < L ? s[kb][i] * a.scale_log2 : -INFINITY;
-            s[kb][i] = v;
-            tmax = fmaxf(tmax, v);
+            if (tile * AKT + s_key(0, i, lane) >= L) s0[i] = -INFINITY;
+            if (tile * AKT + s_key(1, i, lane) >= L) s1[i] = -INFINITY;
           }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mn = fmaxf(m, tmax);
-        const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+        float tmax = s0[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s0[i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
+        const float mn = fmaxf(m, tmax);   // finite: key 0 of the first tile is valid
+        const float alpha = fexp2(m - mn); // 0 on the first tile (m = -inf)
         float sum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = exp2f(s[kb][i] - mn);
-            s[kb][i] = p;
-            sum += p;
-          }
+        for (int i = 0; i < 16; ++i) {
+          s0[i] = fexp2(fmaf(s0[i], c, -mn));
+          s1[i] = fexp2(fmaf(s1[i], c, -mn));
+          sum += s0[i] + s1[i];
+        }
         l = l * alpha + sum;
         m = mn;
+        if (alpha != 1.f) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          pv_chunk(vs, kb, 0, s[kb], o, lane);
-          pv_chunk(vs, kb, 1, s[kb], o, lane);
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
         }
-        if (more) {
-          store_k(lds + ((tile + 1) & 1) * A_STAGE, rk);
-          store_v(lds + ((tile + 1) & 1) * A_STAGE + K_TILE, rv);
-        }
+        pv_chunk(vs, 0, 0, s0, o, lane);
+        pv_chunk(vs, 0, 1, s0, o, lane);
+        pv_chunk(vs, 1, 0, s1, o, lane);
+        pv_chunk(vs, 1, 1, s1, o, lane);
+        store_group<true>(lds + ((tile + 1) & 1) * A_STAGE, wave, lane, tr);
         __syncthreads();
       }
       const float lt = l + __shfl_xor(l, 32);
       store_o(a, q0, row, Q, h, o, 1.f / lt);
       __syncthreads();
     }
+  }
+}
+
+// Longest-processing-time-first order of the sequences (by cache length; equal
+// lengths keep their index order), so the long (sequence, head) items start first.
+__global__ void lpt_order(const int32_t* __restrict__ cu_k, int B, int32_t* __restrict__ order) {
+  for (int bb = threadIdx.x; bb < B; bb += blockDim.x) {
+    const int Lb = cu_k[bb + 1] - cu_k[bb];
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const int Lj = cu_k[j + 1] - cu_k[j];
+      rank += (Lj > Lb) || (Lj == Lb && j < bb);
+    }
+    order[rank] = bb;
   }
 }
 
@@ -486,8 +560,9 @@ __global__ __launch_bounds__(64) void attn_f32(const float* __restrict__ q,
 
 extern "C" size_t fc_attention_workspace_size(int32_t B, int32_t T_q, int32_t T_k, int32_t n_heads,
                                               int32_t head_dim, int32_t with_importance) {
-  (void)B; (void)T_q; (void)T_k; (void)n_heads; (void)head_dim; (void)with_importance;
-  return 0;
+  (void)T_q; (void)T_k; (void)n_heads; (void)head_dim; (void)with_importance;
+  // the longest-first sequence order
+  return B > 0 ? (((size_t)B * sizeof(int32_t) + 255) / 256) * 256 : 0;
 }
 
 extern "C" fc_status_t fc_varlen_bidir_attention(
@@ -497,7 +572,6 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
     int32_t head_dim, float softmax_scale, void* out, float* importance, int32_t accumulate,
     void* workspace, size_t workspace_bytes, int32_t dtype, fc_stream_t stream) {
   fc_clear_error();
-  (void)workspace;
   FC_REQUIRE(B >= 1 && n_heads >= 1 && max_seqlen_q >= 0 && T_k >= 0, FC_ERR_INVALID_VALUE,
              "fc_varlen_bidir_attention: bad sizes B=%d n_heads=%d max_seqlen_q=%d T_k=%d", B,
              n_heads, max_seqlen_q, T_k);
@@ -513,6 +587,8 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
   FC_REQUIRE(workspace_bytes >= fc_attention_workspace_size(B, 0, T_k, n_heads, head_dim,
                                                             importance != nullptr),
              FC_ERR_WORKSPACE, "fc_varlen_bidir_attention: workspace too small");
+  FC_REQUIRE(workspace != nullptr, FC_ERR_WORKSPACE,
+             "fc_varlen_bidir_attention: workspace required (fc_attention_workspace_size)");
   if (max_seqlen_q == 0) return FC_OK;
   hipStream_t st = (hipStream_t)stream;
   const int log2ps = fc_log2i(page_size);
@@ -526,6 +602,7 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
     a.block_table = block_table;
     a.cu_q = cu_seqlens_q;
     a.cu_k = cu_seqlens_k;
+    a.order = (const int32_t*)workspace;
     a.out = (uint16_t*)out;
     a.imp = importance;
     a.maxp = max_pages_per_seq;
@@ -536,10 +613,15 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
     a.n_rt = (max_seqlen_q + AROWS - 1) / AROWS;
     a.accumulate = accumulate ? 1 : 0;
     a.scale_log2 = softmax_scale * LOG2E;
+    hipLaunchKernelGGL(lpt_order, dim3(1), dim3(256), 0, st, cu_seqlens_k, B, (int32_t*)workspace);
+    const bool ps16 = page_size >= 16;
+    const dim3 grid(importance ? B * n_heads : B * n_heads * a.n_rt);
     if (importance) {
-      hipLaunchKernelGGL(attn_bf16_d128<true>, dim3(B * n_heads), dim3(256), 0, st, a);
+      if (ps16) hipLaunchKernelGGL((attn_bf16_d128<true, true>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((attn_bf16_d128<true, false>), grid, dim3(256), 0, st, a);
     } else {
-      hipLaunchKernelGGL(attn_bf16_d128<false>, dim3(B * n_heads * a.n_rt), dim3(256), 0, st, a);
+      if (ps16) hipLaunchKernelGGL((attn_bf16_d128<false, true>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((attn_bf16_d128<false, false>), grid, dim3(256), 0, st, a);
     }
     return fc_check_launch("fc_varlen_bidir_attention");
   }

@@ -4,11 +4,11 @@
 // Q and K with RoPE and writes K and V into the cache in a single pass
 // (infernews post "Flash-dLLM 讓擴散式語言模型解碼更快、更省記憶體", paragraph 2).
 //
-// bf16 path: a 256 x 256 x 64 MFMA GEMM tile (gemm_tile.hpp) whose epilogue works
-// on the fp32 accumulators in registers. Each wave owns 128 output columns, i.e.
-// exactly one head of D = 128, so the rotate-half partners e and e + 64 of a
-// token sit in the same lane and register index of accumulator blocks nb and
-// nb + 2: RoPE needs no data exchange. Rotation angles are formed in fp64 as
+// bf16 path: a 256 x 256 x 64 MFMA GEMM tile with 8 waves (gemm_tile.hpp,
+// Gemm8) whose epilogue works on the fp32 accumulators in registers. A wave's
+// 64 columns are half of one head of D = 128 chosen so that the rotate-half
+// partners e and e + 64 of a token sit in the same lane and register index of
+// its two accumulator blocks: RoPE needs no data exchange. Rotation angles are formed in fp64 as
 // revolutions (pos * base^(-2e/D) / 2pi, fractional part) and fed to the
 // hardware sine/cosine, which take revolutions. Rounded bf16 values go straight
 // to q_out or to the token's cache slot.
@@ -31,16 +31,15 @@ FC_DEVICE int find_seq(const int32_t* __restrict__ cu, int B, int row) {
   return lo;
 }
 
-__global__ __launch_bounds__(256, 1) void qkv_rope_cache_bf16_d128(
+__global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     const uint16_t* __restrict__ hidden, const int32_t* __restrict__ positions,
     const int32_t* __restrict__ cu_q, int B, int M, const uint16_t* __restrict__ w, int d, int H,
     float rope_base, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, int maxp, int log2ps, uint16_t* __restrict__ q_out,
     int32_t* __restrict__ slot_mapping, int n_tiles_n) {
-  using ML = GemmMainloop<QKV_BM, QKV_BN>;
-  using C = ML::C;
+  using G = Gemm8<ColsRopePairs>;
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
 
   // N-tile fastest: consecutive workgroups (spread over the XCDs round-robin)
   // take different weight column blocks, so each XCD streams a disjoint slice of W.
@@ -48,15 +47,15 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_cache_bf16_d128(
   const int mt = blockIdx.x / n_tiles_n;
   const int m0 = mt * QKV_BM, n0 = nt * QKV_BN;
 
-  f32x16_t acc[C::MB][C::NB];
-  ML::run(hidden, d, M, w, d, 3 * d, d, m0, n0, lds, acc);
+  f32x16_t acc[G::MB][G::NB];
+  G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, lds, acc);
 
   // token positions and cache slots of this tile's rows
   int* s_pos = (int*)lds;
   int* s_slot = s_pos + QKV_BM;
   const int t = threadIdx.x;
   const int ps_mask = (1 << log2ps) - 1;
-  {
+  if (t < QKV_BM) {
     const int row = m0 + t;
     int p = 0, slot = 0;
     if (row < M) {
@@ -73,44 +72,38 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_cache_bf16_d128(
   }
   __syncthreads();
 
-  const int wave = t >> 6, lane = t & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int col0 = n0 + wn * C::WN;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63, lr = lane & 31;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int col0 = n0 + (wn >> 1) * D;      // first column of this wave's head
   const int region = col0 / d;              // 0 = Q, 1 = K, 2 = V
   const int h = (col0 - region * d) / D;
+  const int e = (wn & 1) * 32 + lr;         // rotation pair (e, e + 64) of this lane
 
   if (region < 2) {
-    double frev[2];
-    const double l2b = log2((double)rope_base);
+    const double frev = exp2(-2.0 * (double)e / (double)D * log2((double)rope_base)) *
+                        0.15915494309189535;  // turns per position: inv_freq / 2pi
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int e = nb * 32 + (lane & 31);
-      frev[nb] = exp2(-2.0 * (double)e / (double)D * l2b) * 0.15915494309189535;  // / 2pi
-    }
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+    for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int pos = s_pos[wm * C::WM + acc_row(mb, i, lane)];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          double r = (double)pos * frev[nb];
-          r -= floor(r);
-          const float rf = (float)r;
-          const float cs = __builtin_amdgcn_cosf(rf), sn = __builtin_amdgcn_sinf(rf);
-          const float x = acc[mb][nb][i], y = acc[mb][nb + 2][i];
-          acc[mb][nb][i] = x * cs - y * sn;
-          acc[mb][nb + 2][i] = y * cs + x * sn;
-        }
+        const int pos = s_pos[wm * 128 + acc_row(mb, i, lane)];
+        double r = (double)pos * frev;
+        r -= floor(r);
+        const float rf = (float)r;
+        const float cs = __builtin_amdgcn_cosf(rf), sn = __builtin_amdgcn_sinf(rf);
+        const float x = acc[mb][0][i], y = acc[mb][1][i];
+        acc[mb][0][i] = x * cs - y * sn;
+        acc[mb][1][i] = y * cs + x * sn;
       }
   }
 
   uint16_t* cache = region == 1 ? kc : vc;
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
+  for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int rl = wm * C::WM + acc_row(mb, i, lane);
+      const int rl = wm * 128 + acc_row(mb, i, lane);
       const int row = m0 + rl;
       if (row >= M) continue;
       uint16_t* dst;
@@ -120,8 +113,8 @@ __global__ __launch_bounds__(256, 1) void qkv_rope_cache_bf16_d128(
         const int slot = s_slot[rl];
         dst = cache + (((size_t)(slot >> log2ps) * H + h) * (ps_mask + 1) + (slot & ps_mask)) * D;
       }
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) dst[acc_col(nb, lane)] = f32_to_bf16(acc[mb][nb][i]);
+      dst[e] = f32_to_bf16(acc[mb][0][i]);
+      dst[e + 64] = f32_to_bf16(acc[mb][1][i]);
     }
 }
 
@@ -218,7 +211,7 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
                FC_ERR_UNSUPPORTED, "fc_qkv_rope_cache_write: operands above 2 GiB");
     const int n_tiles_n = (write_cache ? 3 * d_model : d_model) / QKV_BN;
     const int n_tiles_m = (T_q + QKV_BM - 1) / QKV_BM;
-    hipLaunchKernelGGL(qkv_rope_cache_bf16_d128, dim3(n_tiles_m * n_tiles_n), dim3(256), 0, st,
+    hipLaunchKernelGGL(qkv_rope_cache_bf16_d128, dim3(n_tiles_m * n_tiles_n), dim3(512), 0, st,
                        (const uint16_t*)hidden, positions, cu_seqlens_q, B, T_q,
                        (const uint16_t*)w_qkv, d_model, n_heads, rope_base, (uint16_t*)k_cache,
                        (uint16_t*)v_cache, block_table, max_pages_per_seq, log2ps,

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int TK_THREADS = 256;
+constexpr int TK_THREADS = 1024;
 
 FC_DEVICE uint32_t order_key(float s) {
   if (s == 0.f) s = 0.f;  // one key for +0 and -0
@@ -69,11 +69,21 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     return;
   }
 
-  // 1. head-summed scores and candidate flags
+  // 1. head-summed scores (heads added in ascending order) and candidate flags;
+  //    eight loads are issued before their additions
   int my_cand = 0;
   for (int j = t; j < L; j += TK_THREADS) {
+    const float* src = imp + k0 + j;
     float s = 0.f;
-    for (int h = 0; h < H; ++h) s += imp[(size_t)h * T_k + k0 + j];
+    int h = 0;
+    for (; h + 8 <= H; h += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = src[(size_t)(h + u) * T_k];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += x[u];
+    }
+    for (; h < H; ++h) s += src[(size_t)h * T_k];
     s_score[j] = s;
     const uint8_t c = cand_mask ? (uint8_t)(cand_mask[k0 + j] != 0) : (uint8_t)1;
     s_cand[j] = c;

@@ -92,7 +92,7 @@ def test_attention_argument_checks():
     base = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, block_table=FAKE, max_pages_per_seq=4,
                 page_size=16, cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, B=2, max_seqlen_q=8, T_k=64,
                 n_heads=2, head_dim=128, softmax_scale=0.088, out=FAKE, importance=FAKE,
-                accumulate=0, workspace=None, workspace_bytes=0, dtype=fc.FC_DTYPE_BF16)
+                accumulate=0, workspace=FAKE, workspace_bytes=1 << 20, dtype=fc.FC_DTYPE_BF16)
 
     def expect(name, **over):
         a = dict(base)
@@ -107,7 +107,10 @@ def test_attention_argument_checks():
     expect("FC_ERR_INVALID_VALUE", softmax_scale=0.0)
     expect("FC_ERR_INVALID_VALUE", dtype=3)
     expect("FC_ERR_UNSUPPORTED", head_dim=64)
-    assert fc.fc_attention_workspace_size(2, 8, 64, 2, 128, 1) >= 0
+    need = fc.fc_attention_workspace_size(2, 8, 64, 2, 128, 1)
+    assert need >= 2 * 4
+    expect("FC_ERR_WORKSPACE", workspace_bytes=need - 1)
+    expect("FC_ERR_WORKSPACE", workspace=None)
     a = dict(base)
     a.update(max_seqlen_q=0)
     fc.fc_varlen_bidir_attention(**a, stream=0)   # empty query: returns OK, enqueues nothing
