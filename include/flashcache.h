@@ -105,6 +105,9 @@ const char* fc_version(void);
  *                                   of a sequence are never read)
  * q_out         [T_q, H, D]         dtype
  * slot_mapping  [T_q] or NULL
+ * workspace     device memory of at least fc_qkv_workspace_size() bytes (the
+ *               per-token rotation table; overwritten; NULL allowed when that
+ *               size is 0; calls that overlap on one workspace race)
  * Supported: bf16 with D = 128 and d a multiple of 256; f32 with D in {64,128}.
  * page_size must be a power of two in [1, 256].
  */
@@ -113,7 +116,10 @@ fc_status_t fc_qkv_rope_cache_write(
     int32_t T_q, const void* w_qkv, int32_t d_model, int32_t n_heads, int32_t head_dim,
     float rope_base, void* k_cache, void* v_cache, const int32_t* block_table,
     int32_t max_pages_per_seq, int32_t page_size, void* q_out, int32_t* slot_mapping,
-    int32_t dtype, fc_stream_t stream);
+    void* workspace, size_t workspace_bytes, int32_t dtype, fc_stream_t stream);
+
+/* Bytes of device workspace fc_qkv_rope_cache_write needs (0 when none). */
+size_t fc_qkv_workspace_size(int32_t T_q, int32_t head_dim, int32_t dtype);
 
 /* Bytes of device workspace fc_varlen_bidir_attention needs for these sizes
  * (0 when none). */

@@ -161,11 +161,16 @@ FC_DEVICE void store_group(char* stage, int g, int lane, const TileRegs& r) {
 
 // ---- MFMA pieces -----------------------------------------------------------
 // S^T block kb (keys kb*32 .. +31 of the tile) for this wave's 32 queries.
+// The MFMA runs are issued at raised wave priority: with two workgroups per CU
+// the wave that is feeding the matrix unit wins issue arbitration over the
+// other wave's softmax arithmetic.
 FC_DEVICE f32x16_t s_block(const char* ks, int kb, const bf16x8_t (&qf)[8], int lane) {
   f32x16_t s = {};
   const char* row = ks + (kb * 32 + (lane & 31)) * K_STRIDE + (lane >> 5) * 16;
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) s = mfma32x32x16(as_bf16x8(*(const u32x4_t*)(row + kc * 32)), qf[kc], s);
+  __builtin_amdgcn_s_setprio(0);
   return s;
 }
 
@@ -182,6 +187,7 @@ FC_DEVICE void pv_chunk(const char* vs, int kb, int c, const f32x16_t& p, f32x16
   for (int w = 0; w < 4; ++w) pb[w] = pack2(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
   const bf16x8_t bop = as_bf16x8(pb);
   const int kbase = kb * 32 + c * 16 + (lane >> 5) * 4;
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const char* row = vs + (db * 32 + (lane & 31)) * V_STRIDE + kbase * 2;
@@ -191,6 +197,7 @@ FC_DEVICE void pv_chunk(const char* vs, int kb, int c, const f32x16_t& p, f32x16
     av[0] = x0[0]; av[1] = x0[1]; av[2] = x1[0]; av[3] = x1[1];
     o[db] = mfma32x32x16(as_bf16x8(av), bop, o[db]);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 FC_DEVICE void load_q(const AttnArgs& a, int q0, int row, int Q, int h, bf16x8_t (&qf)[8]) {

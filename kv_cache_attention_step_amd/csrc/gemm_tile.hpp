@@ -190,9 +190,14 @@ struct Gemm8 {
     }
   }
 
+  // The MFMA cluster runs at raised wave priority: of the two waves sharing a
+  // SIMD, the one feeding the matrix unit wins issue arbitration, which
+  // staggers the pair so one wave's loads and barrier wait overlap the other's
+  // MFMAs.
   static FC_DEVICE void compute(const char* stage, int wm, int wn, f32x16_t (&acc)[MB][NB]) {
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, hb = lane >> 5;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int chunk = kk * 2 + hb;
@@ -208,6 +213,7 @@ struct Gemm8 {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32x32x16(af[mb], bfr[nb], acc[mb][nb]);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // K must be a multiple of 64. Ends on a barrier. The prefetch loads and LDS

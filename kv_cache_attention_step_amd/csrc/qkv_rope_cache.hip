@@ -9,9 +9,10 @@
 // 64 columns are half of one head of D = 128 chosen so that the rotate-half
 // partners e and e + 64 of a token sit in the same lane and register index of
 // its two accumulator blocks: RoPE needs no data exchange. Rotation angles are formed in fp64 as
-// revolutions (pos * base^(-2e/D) / 2pi, fractional part) and fed to the
-// hardware sine/cosine, which take revolutions. Rounded bf16 values go straight
-// to q_out or to the token's cache slot.
+// The rotation (cos, sin) per (token, pair) comes from a small table computed
+// first in fp64 (rope_table_kernel), so the angle work is done once per token
+// instead of once per head. Rounded bf16 values go straight to q_out or to the
+// token's cache slot.
 //
 // f32 path (small models): one work-item per (token, head, rotation pair).
 #include "gemm_tile.hpp"
@@ -31,12 +32,26 @@ FC_DEVICE int find_seq(const int32_t* __restrict__ cu, int B, int row) {
   return lo;
 }
 
+// Rotation table: rope[t][e] = (cos, sin) of positions[t] * base^(-2e/D), in
+// fp64 then rounded to fp32. One entry per (token, pair); every Q and K head
+// of the token reuses it.
+__global__ void rope_table_kernel(const int32_t* __restrict__ positions, int T, int half,
+                                  float rope_base, float2* __restrict__ table) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * half) return;
+  const int t = idx / half, e = idx - t * half;
+  const double inv_freq = exp2(-(double)e / (double)half * log2((double)rope_base));
+  double sn, cs;
+  sincos((double)positions[t] * inv_freq, &sn, &cs);
+  table[idx] = make_float2((float)cs, (float)sn);
+}
+
 __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     const uint16_t* __restrict__ hidden, const int32_t* __restrict__ positions,
     const int32_t* __restrict__ cu_q, int B, int M, const uint16_t* __restrict__ w, int d, int H,
     float rope_base, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, int maxp, int log2ps, uint16_t* __restrict__ q_out,
-    int32_t* __restrict__ slot_mapping, int n_tiles_n) {
+    int32_t* __restrict__ slot_mapping, const float2* __restrict__ rope, int n_tiles_n) {
   using G = Gemm8<ColsRopePairs>;
   constexpr int D = 128;
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
@@ -81,20 +96,15 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
   const int e = (wn & 1) * 32 + lr;         // rotation pair (e, e + 64) of this lane
 
   if (region < 2) {
-    const double frev = exp2(-2.0 * (double)e / (double)D * log2((double)rope_base)) *
-                        0.15915494309189535;  // turns per position: inv_freq / 2pi
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int pos = s_pos[wm * 128 + acc_row(mb, i, lane)];
-        double r = (double)pos * frev;
-        r -= floor(r);
-        const float rf = (float)r;
-        const float cs = __builtin_amdgcn_cosf(rf), sn = __builtin_amdgcn_sinf(rf);
+        const int row = min(m0 + wm * 128 + acc_row(mb, i, lane), M - 1);
+        const float2 cs = rope[(size_t)row * (D / 2) + e];
         const float x = acc[mb][0][i], y = acc[mb][1][i];
-        acc[mb][0][i] = x * cs - y * sn;
-        acc[mb][1][i] = y * cs + x * sn;
+        acc[mb][0][i] = x * cs.x - y * cs.y;
+        acc[mb][1][i] = y * cs.x + x * cs.y;
       }
   }
 
@@ -171,12 +181,17 @@ __global__ void qkv_rope_cache_f32(const float* __restrict__ hidden,
 
 }  // namespace
 
+extern "C" size_t fc_qkv_workspace_size(int32_t T_q, int32_t head_dim, int32_t dtype) {
+  if (dtype != FC_DTYPE_BF16 || T_q <= 0 || head_dim <= 0) return 0;
+  return (((size_t)T_q * (head_dim / 2) * sizeof(float2)) + 255) / 256 * 256;
+}
+
 extern "C" fc_status_t fc_qkv_rope_cache_write(
     const void* hidden, const int32_t* positions, const int32_t* cu_seqlens_q, int32_t B,
     int32_t T_q, const void* w_qkv, int32_t d_model, int32_t n_heads, int32_t head_dim,
     float rope_base, void* k_cache, void* v_cache, const int32_t* block_table,
     int32_t max_pages_per_seq, int32_t page_size, void* q_out, int32_t* slot_mapping,
-    int32_t dtype, fc_stream_t stream) {
+    void* workspace, size_t workspace_bytes, int32_t dtype, fc_stream_t stream) {
   fc_clear_error();
   FC_REQUIRE(B >= 1, FC_ERR_INVALID_VALUE, "fc_qkv_rope_cache_write: B=%d must be >= 1", B);
   FC_REQUIRE(T_q >= 0, FC_ERR_INVALID_VALUE, "fc_qkv_rope_cache_write: T_q=%d < 0", T_q);
@@ -209,13 +224,19 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
     FC_REQUIRE((int64_t)T_q * d_model * 2 < (1ll << 31) &&
                    (int64_t)3 * d_model * d_model * 2 < (1ll << 31),
                FC_ERR_UNSUPPORTED, "fc_qkv_rope_cache_write: operands above 2 GiB");
+    FC_REQUIRE(workspace && workspace_bytes >= fc_qkv_workspace_size(T_q, head_dim, dtype),
+               FC_ERR_WORKSPACE, "fc_qkv_rope_cache_write: workspace of %zu bytes required",
+               fc_qkv_workspace_size(T_q, head_dim, dtype));
     const int n_tiles_n = (write_cache ? 3 * d_model : d_model) / QKV_BN;
     const int n_tiles_m = (T_q + QKV_BM - 1) / QKV_BM;
+    const int n_rot = T_q * (head_dim / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((n_rot + 255) / 256), dim3(256), 0, st, positions,
+                       T_q, head_dim / 2, rope_base, (float2*)workspace);
     hipLaunchKernelGGL(qkv_rope_cache_bf16_d128, dim3(n_tiles_m * n_tiles_n), dim3(512), 0, st,
                        (const uint16_t*)hidden, positions, cu_seqlens_q, B, T_q,
                        (const uint16_t*)w_qkv, d_model, n_heads, rope_base, (uint16_t*)k_cache,
                        (uint16_t*)v_cache, block_table, max_pages_per_seq, log2ps,
-                       (uint16_t*)q_out, slot_mapping, n_tiles_n);
+                       (uint16_t*)q_out, slot_mapping, (const float2*)workspace, n_tiles_n);
     return fc_check_launch("fc_qkv_rope_cache_write");
   }
   FC_REQUIRE(head_dim == 64 || head_dim == 128, FC_ERR_UNSUPPORTED,

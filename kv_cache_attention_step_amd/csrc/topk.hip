@@ -106,14 +106,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         if ((key & prefix_mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1);
       }
       __syncthreads();
-      if (t == 0) {
-        int acc = 0, bin = 255;
-        for (; bin > 0; --bin) {
-          if (acc + s_hist[bin] >= need) break;
-          acc += s_hist[bin];
-        }
-        s_ctl[0] = bin;
-        s_ctl[1] = need - acc;
+      // bins from the top: cum = number of keys in bins >= 255 - t; the chosen
+      // bin is the first (highest) one where cum reaches `need`
+      const int hcount = t < 256 ? s_hist[255 - t] : 0;
+      int below;
+      block_exclusive_scan(hcount, s_scan, &below);
+      if (t < 256 && below < need && below + hcount >= need) {
+        s_ctl[0] = 255 - t;
+        s_ctl[1] = need - below;
       }
       __syncthreads();
       prefix |= (uint32_t)s_ctl[0] << shift;

@@ -83,6 +83,9 @@ class StepBuffers:
         ws = fc.fc_attention_workspace_size(self.B, self.T_q, self.T_k, self.H, self.D, 1)
         self.ws_bytes = ws
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws else None
+        qws = fc.fc_qkv_workspace_size(self.T_q, self.D, self.dtype)
+        self.qkv_ws_bytes = qws
+        self.qkv_workspace = torch.empty(qws, dtype=torch.uint8, device=device) if qws else None
         self.max_seqlen_q = inp.max_seqlen_q
         self.scale = 1.0 / math.sqrt(self.D)
 
@@ -92,7 +95,8 @@ class StepBuffers:
         fc.fc_qkv_rope_cache_write(self.hidden, self.positions, self.cu_q, self.B, self.T_q,
                                    self.w_qkv, self.d, self.H, self.D, cfg.rope_base, self.k_cache,
                                    self.v_cache, self.block_table, self.inp.max_pages,
-                                   cfg.page_size, self.q_out, self.slot_mapping, self.dtype, stream)
+                                   cfg.page_size, self.q_out, self.slot_mapping, self.qkv_workspace,
+                                   self.qkv_ws_bytes, self.dtype, stream)
 
     def attention(self, stream=None, importance=True, accumulate=False):
         fc.fc_varlen_bidir_attention(self.q_out, self.k_cache, self.v_cache, self.block_table,
@@ -145,7 +149,7 @@ class VerifyBuffers:
         fc.fc_qkv_rope_cache_write(s.hidden, s.positions, s.cu_q, s.B, s.T_q, s.w_qkv, s.d, s.H,
                                    s.D, s.cfg.rope_base, None, None, s.block_table,
                                    s.inp.max_pages, s.cfg.page_size, s.q_out, s.slot_mapping,
-                                   s.dtype, stream)
+                                   s.qkv_workspace, s.qkv_ws_bytes, s.dtype, stream)
 
     def attention(self, stream=None):
         self.step.attention(stream, importance=False)

@@ -60,7 +60,8 @@ def test_qkv_argument_checks():
     base = dict(hidden=FAKE, positions=FAKE, cu_seqlens_q=FAKE, B=1, T_q=4, w_qkv=FAKE,
                 d_model=256, n_heads=2, head_dim=128, rope_base=1e4, k_cache=FAKE, v_cache=FAKE,
                 block_table=FAKE, max_pages_per_seq=4, page_size=16, q_out=FAKE,
-                slot_mapping=None, dtype=fc.FC_DTYPE_BF16)
+                slot_mapping=None, workspace=FAKE, workspace_bytes=1 << 20,
+                dtype=fc.FC_DTYPE_BF16)
 
     def call(**over):
         a = dict(base)
@@ -83,6 +84,11 @@ def test_qkv_argument_checks():
     expect("FC_ERR_UNSUPPORTED", n_heads=4, head_dim=64)    # bf16 supports D = 128 only
     expect("FC_ERR_UNSUPPORTED", n_heads=3, d_model=384)    # d % 256 != 0
     expect("FC_ERR_UNSUPPORTED", dtype=fc.FC_DTYPE_F32, n_heads=8, head_dim=32)
+    need = fc.fc_qkv_workspace_size(4, 128, fc.FC_DTYPE_BF16)
+    assert need >= 4 * 64 * 8
+    expect("FC_ERR_WORKSPACE", workspace_bytes=need - 1)
+    expect("FC_ERR_WORKSPACE", workspace=None)
+    assert fc.fc_qkv_workspace_size(4, 64, fc.FC_DTYPE_F32) == 0
     # nothing to do is not an error
     call(T_q=0)(0)
 

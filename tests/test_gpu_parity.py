@@ -97,6 +97,15 @@ def test_small_bf16_varlen_step_with_nan_tails(torch_cuda):
     full_parity(inp, got)
 
 
+def test_small_page_size_path(torch_cuda):
+    """page_size 4 (< 16 keys of a load group span several pages)."""
+    cfg = dataclasses.replace(SMALL_BF16, name="C2-ps4", seed=24, page_size=4)
+    _say("case C2-small bf16, page size 4, NaN tails")
+    inp = W.make_step_inputs(cfg, tail_nan=True)
+    got = run_gpu_step(inp, torch_cuda)
+    full_parity(inp, got)
+
+
 def test_bf16_query_longer_than_one_row_tile(torch_cuda):
     """Q_b > 128 rows: the importance path loops over row tiles in one workgroup."""
     cfg = dataclasses.replace(SMALL_BF16, name="C2-rows", seed=22, batch=2, prompt=(100, 180),
