@@ -105,6 +105,10 @@ const char* fc_version(void);
  *                                   of a sequence are never read)
  * q_out         [T_q, H, D]         dtype
  * slot_mapping  [T_q] or NULL
+ * row_scale     [T_q] fp32 or NULL: when set, token t's q, k and v are
+ *               multiplied by row_scale[t] before RoPE, i.e. the projection of
+ *               hidden[t] * row_scale[t] (an input normalisation computed by
+ *               fc_rms_row_scale)
  * workspace     device memory of at least fc_qkv_workspace_size() bytes (the
  *               per-token rotation table; overwritten; NULL allowed when that
  *               size is 0; calls that overlap on one workspace race)
@@ -116,7 +120,8 @@ fc_status_t fc_qkv_rope_cache_write(
     int32_t T_q, const void* w_qkv, int32_t d_model, int32_t n_heads, int32_t head_dim,
     float rope_base, void* k_cache, void* v_cache, const int32_t* block_table,
     int32_t max_pages_per_seq, int32_t page_size, void* q_out, int32_t* slot_mapping,
-    void* workspace, size_t workspace_bytes, int32_t dtype, fc_stream_t stream);
+    const float* row_scale, void* workspace, size_t workspace_bytes, int32_t dtype,
+    fc_stream_t stream);
 
 /* Bytes of device workspace fc_qkv_rope_cache_write needs (0 when none). */
 size_t fc_qkv_workspace_size(int32_t T_q, int32_t head_dim, int32_t dtype);
@@ -209,6 +214,17 @@ fc_status_t fv_verify_accept(
     const void* logits, int32_t vocab, const int32_t* cu_positions, int32_t B, int32_t R,
     const int32_t* draft_tokens, float tau, int32_t* argmax, float* conf, uint8_t* accept_row,
     uint8_t* accept_pos, fc_stream_t stream);
+
+/*
+ * Per-row RMS normalisation factor for a layer's input in the layer stack:
+ * scale[m] = 1 / sqrt(mean_n x[m, n]^2 + eps) (fp32 accumulation, no learned
+ * weight). Feeds row_scale of fc_qkv_rope_cache_write. Not part of the pages'
+ * single-step description: a stack of residual layers with random weights needs
+ * it to keep the hidden state bounded, as pre-normalised transformer layers do.
+ * x [M, N] dtype, scale [M] fp32.
+ */
+fc_status_t fc_rms_row_scale(const void* x, int32_t M, int32_t N, float eps, float* scale,
+                             int32_t dtype, fc_stream_t stream);
 
 /*
  * Output projection with residual for the layer stack: h_inout += x . w^T

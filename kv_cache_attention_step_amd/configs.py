@@ -47,6 +47,7 @@ class StepConfig:
     hidden_std: float = 1.0
     weight_std: float = 0.02
     cache_len_fixed: Optional[int] = None  # C4: every cache has this length
+    rms_eps: float = 1e-5           # layer-input RMS normalisation of the layer stack
     extra: dict = field(default_factory=dict)
 
     @property

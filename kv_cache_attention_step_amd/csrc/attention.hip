@@ -365,8 +365,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
       const float mf = fmaxf(m, mo);
       const float lf = (m == -INFINITY ? 0.f : l * fexp2(m - mf)) +
                        (mo == -INFINITY ? 0.f : lo * fexp2(mo - mf));
-      // P = exp2(s c - mf) / lf = exp2(s c - (mf + log2 lf)); rows past Q get P = 0
-      const float mf2 = row_ok ? mf + __log2f(lf) : INFINITY;
+      // P = exp2(s c - mf) * (1 / lf); rows past Q get P = 0
+      const float inv_l = row_ok ? 1.f / lf : 0.f;
 
       // ---------------- pass 2: P, O += P V, importance ----------------
       load_group<PS_GE16, true>(a, bt, h, 0, L, wave, lane, tr);
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb) {
           f32x16_t s = s_block(ks, kb, qf, lane);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[i] = fexp2(fmaf(s[i], c, -mf2));
+          for (int i = 0; i < 16; ++i) s[i] = fexp2(fmaf(s[i], c, -mf)) * inv_l;
           if (ragged && !more) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)

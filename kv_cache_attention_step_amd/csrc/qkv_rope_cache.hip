@@ -51,7 +51,8 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     const int32_t* __restrict__ cu_q, int B, int M, const uint16_t* __restrict__ w, int d, int H,
     float rope_base, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, int maxp, int log2ps, uint16_t* __restrict__ q_out,
-    int32_t* __restrict__ slot_mapping, const float2* __restrict__ rope, int n_tiles_n) {
+    int32_t* __restrict__ slot_mapping, const float2* __restrict__ rope,
+    const float* __restrict__ row_scale, int n_tiles_n) {
   using G = Gemm8<ColsRopePairs>;
   constexpr int D = 128;
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
@@ -95,6 +96,16 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
   const int h = (col0 - region * d) / D;
   const int e = (wn & 1) * 32 + lr;         // rotation pair (e, e + 64) of this lane
 
+  if (row_scale) {  // per-token input normalisation: (x r) W^T = r (x W^T)
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float r = row_scale[min(m0 + wm * 128 + acc_row(mb, i, lane), M - 1)];
+        acc[mb][0][i] *= r;
+        acc[mb][1][i] *= r;
+      }
+  }
   if (region < 2) {
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb)
@@ -136,7 +147,8 @@ __global__ void qkv_rope_cache_f32(const float* __restrict__ hidden,
                                    const float* __restrict__ w, int d, int H, int D,
                                    float rope_base, float* __restrict__ kc, float* __restrict__ vc,
                                    const int32_t* __restrict__ block_table, int maxp, int log2ps,
-                                   float* __restrict__ q_out, int32_t* __restrict__ slot_mapping) {
+                                   float* __restrict__ q_out, int32_t* __restrict__ slot_mapping,
+                                   const float* __restrict__ row_scale) {
   const int row = blockIdx.x;
   const int region = blockIdx.y / H;
   const int h = blockIdx.y % H;
@@ -150,6 +162,10 @@ __global__ void qkv_rope_cache_f32(const float* __restrict__ hidden,
     const float xv = x[c];
     a0 = fmaf(xv, w0[c], a0);
     a1 = fmaf(xv, w1[c], a1);
+  }
+  if (row_scale) {
+    a0 *= row_scale[row];
+    a1 *= row_scale[row];
   }
   const int p = positions[row];
   if (region < 2) {
@@ -179,7 +195,47 @@ __global__ void qkv_rope_cache_f32(const float* __restrict__ hidden,
   dst[e + half] = a1;
 }
 
+// 1 / sqrt(mean(x^2) + eps) per row; one workgroup per row, fixed reduction order.
+template <typename T>
+__global__ __launch_bounds__(256) void rms_row_scale_kernel(const T* __restrict__ x, int N, float eps,
+                                                            float* __restrict__ scale) {
+  __shared__ float part[256 / 64];
+  const T* row = x + (size_t)blockIdx.x * N;
+  float s = 0.f;
+  for (int c = threadIdx.x; c < N; c += 256) {
+    float v;
+    if constexpr (sizeof(T) == 2) v = bf16_to_f32(row[c]); else v = row[c];
+    s = fmaf(v, v, s);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    scale[blockIdx.x] = 1.f / sqrtf(tot / (float)N + eps);
+  }
+}
+
 }  // namespace
+
+extern "C" fc_status_t fc_rms_row_scale(const void* x, int32_t M, int32_t N, float eps,
+                                        float* scale, int32_t dtype, fc_stream_t stream) {
+  fc_clear_error();
+  FC_REQUIRE(M >= 0 && N >= 1 && eps >= 0.f, FC_ERR_INVALID_VALUE,
+             "fc_rms_row_scale: bad sizes M=%d N=%d eps=%g", M, N, (double)eps);
+  FC_REQUIRE(dtype == FC_DTYPE_BF16 || dtype == FC_DTYPE_F32, FC_ERR_INVALID_VALUE,
+             "fc_rms_row_scale: unknown dtype %d", dtype);
+  if (M == 0) return FC_OK;
+  FC_REQUIRE(x && scale, FC_ERR_INVALID_VALUE, "fc_rms_row_scale: NULL required pointer");
+  if (dtype == FC_DTYPE_BF16)
+    hipLaunchKernelGGL(rms_row_scale_kernel<uint16_t>, dim3(M), dim3(256), 0, (hipStream_t)stream,
+                       (const uint16_t*)x, N, eps, scale);
+  else
+    hipLaunchKernelGGL(rms_row_scale_kernel<float>, dim3(M), dim3(256), 0, (hipStream_t)stream,
+                       (const float*)x, N, eps, scale);
+  return fc_check_launch("fc_rms_row_scale");
+}
 
 extern "C" size_t fc_qkv_workspace_size(int32_t T_q, int32_t head_dim, int32_t dtype) {
   if (dtype != FC_DTYPE_BF16 || T_q <= 0 || head_dim <= 0) return 0;
@@ -191,7 +247,8 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
     int32_t T_q, const void* w_qkv, int32_t d_model, int32_t n_heads, int32_t head_dim,
     float rope_base, void* k_cache, void* v_cache, const int32_t* block_table,
     int32_t max_pages_per_seq, int32_t page_size, void* q_out, int32_t* slot_mapping,
-    void* workspace, size_t workspace_bytes, int32_t dtype, fc_stream_t stream) {
+    const float* row_scale, void* workspace, size_t workspace_bytes, int32_t dtype,
+    fc_stream_t stream) {
   fc_clear_error();
   FC_REQUIRE(B >= 1, FC_ERR_INVALID_VALUE, "fc_qkv_rope_cache_write: B=%d must be >= 1", B);
   FC_REQUIRE(T_q >= 0, FC_ERR_INVALID_VALUE, "fc_qkv_rope_cache_write: T_q=%d < 0", T_q);
@@ -236,7 +293,8 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
                        (const uint16_t*)hidden, positions, cu_seqlens_q, B, T_q,
                        (const uint16_t*)w_qkv, d_model, n_heads, rope_base, (uint16_t*)k_cache,
                        (uint16_t*)v_cache, block_table, max_pages_per_seq, log2ps,
-                       (uint16_t*)q_out, slot_mapping, (const float2*)workspace, n_tiles_n);
+                       (uint16_t*)q_out, slot_mapping, (const float2*)workspace, row_scale,
+                       n_tiles_n);
     return fc_check_launch("fc_qkv_rope_cache_write");
   }
   FC_REQUIRE(head_dim == 64 || head_dim == 128, FC_ERR_UNSUPPORTED,
@@ -245,6 +303,6 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
                      dim3(head_dim / 2), 0, st, (const float*)hidden, positions, cu_seqlens_q, B,
                      (const float*)w_qkv, d_model, n_heads, head_dim, rope_base, (float*)k_cache,
                      (float*)v_cache, block_table, max_pages_per_seq, log2ps, (float*)q_out,
-                     slot_mapping);
+                     slot_mapping, row_scale);
   return fc_check_launch("fc_qkv_rope_cache_write");
 }

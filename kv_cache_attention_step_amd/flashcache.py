@@ -25,7 +25,7 @@ _STATUS = {0: "FC_OK", 1: "FC_ERR_INVALID_VALUE", 2: "FC_ERR_UNSUPPORTED", 3: "F
 EXPORTS = ("fc_status_string", "fc_last_error", "fc_version", "fc_qkv_rope_cache_write",
            "fc_qkv_workspace_size",
            "fc_attention_workspace_size", "fc_varlen_bidir_attention", "fc_importance_topk",
-           "fv_verify_accept", "fc_linear_residual", "fc_assemble_query")
+           "fv_verify_accept", "fc_linear_residual", "fc_assemble_query", "fc_rms_row_scale")
 
 
 class FlashCacheError(RuntimeError):
@@ -47,7 +47,8 @@ _SIGS = {
     "fc_last_error": ([], ctypes.c_char_p),
     "fc_version": ([], ctypes.c_char_p),
     "fc_qkv_rope_cache_write": ([P, P, P, I32, I32, P, I32, I32, I32, F32, P, P, P, I32, I32, P, P,
-                                 P, SZ, I32, P], I32),
+                                 P, P, SZ, I32, P], I32),
+    "fc_rms_row_scale": ([P, I32, I32, F32, P, I32, P], I32),
     "fc_qkv_workspace_size": ([I32, I32, I32], SZ),
     "fc_attention_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
     "fc_varlen_bidir_attention": ([P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, F32, P, P,
@@ -112,13 +113,18 @@ def fc_qkv_workspace_size(T_q, head_dim, dtype) -> int:
 def fc_qkv_rope_cache_write(hidden, positions, cu_seqlens_q, B, T_q, w_qkv, d_model, n_heads,
                             head_dim, rope_base, k_cache, v_cache, block_table, max_pages_per_seq,
                             page_size, q_out, slot_mapping, workspace, workspace_bytes, dtype,
-                            stream=None):
+                            stream=None, row_scale=None):
     st = load().fc_qkv_rope_cache_write(
         _p(hidden), _p(positions), _p(cu_seqlens_q), B, T_q, _p(w_qkv), d_model, n_heads,
         head_dim, rope_base, _p(k_cache), _p(v_cache), _p(block_table), max_pages_per_seq,
-        page_size, _p(q_out), _p(slot_mapping), _p(workspace), workspace_bytes, dtype,
-        _stream(stream))
+        page_size, _p(q_out), _p(slot_mapping), _p(row_scale), _p(workspace), workspace_bytes,
+        dtype, _stream(stream))
     _check("fc_qkv_rope_cache_write", st)
+
+
+def fc_rms_row_scale(x, M, N, eps, scale, dtype, stream=None):
+    st = load().fc_rms_row_scale(_p(x), M, N, eps, _p(scale), dtype, _stream(stream))
+    _check("fc_rms_row_scale", st)
 
 
 def fc_attention_workspace_size(B, T_q, T_k, n_heads, head_dim, with_importance) -> int:

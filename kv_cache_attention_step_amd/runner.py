@@ -11,6 +11,7 @@ from typing import Dict, Optional
 import numpy as np
 
 from . import flashcache as fc
+from . import workload as W
 from .configs import StepConfig
 from .workload import StepInputs, VerifyInputs
 
@@ -130,7 +131,7 @@ class VerifyBuffers:
     def __init__(self, vi: VerifyInputs, device="cuda"):
         torch = _torch()
         self.vi = vi
-        self.step = StepBuffers(vi.step, device)
+        self.step = StepBuffers(vi.step, device) if vi.step.k_cache.size else None
         cfg = vi.cfg
         self.V = cfg.vocab
         self.tau = cfg.tau
@@ -139,6 +140,7 @@ class VerifyBuffers:
         self.cu_p = to_device(vi.cu_positions, device)
         self.draft = to_device(vi.draft, device)
         self.logits = to_device(vi.logits, device) if vi.logits is not None else None
+        self.B = cfg.batch
         self.argmax = torch.empty(self.R, dtype=torch.int32, device=device)
         self.conf = torch.empty(self.R, dtype=torch.float32, device=device)
         self.accept_row = torch.empty(self.R, dtype=torch.uint8, device=device)
@@ -155,7 +157,7 @@ class VerifyBuffers:
         self.step.attention(stream, importance=False)
 
     def verify(self, stream=None):
-        fc.fv_verify_accept(self.logits, self.V, self.cu_p, self.step.B, self.R, self.draft,
+        fc.fv_verify_accept(self.logits, self.V, self.cu_p, self.B, self.R, self.draft,
                             self.tau, self.argmax, self.conf, self.accept_row, self.accept_pos,
                             stream)
 
@@ -166,6 +168,111 @@ class VerifyBuffers:
 
     def fetch(self):
         out = dict(argmax=to_host(self.argmax), conf=to_host(self.conf),
-                   accept_row=to_host(self.accept_row), accept_pos=to_host(self.accept_pos),
-                   q_out=to_host(self.step.q_out), attn_out=to_host(self.step.attn_out))
+                   accept_row=to_host(self.accept_row), accept_pos=to_host(self.accept_pos))
+        if self.step is not None:
+            out.update(q_out=to_host(self.step.q_out), attn_out=to_host(self.step.attn_out))
         return out
+
+
+class LayerStackDriver:
+    """Block-wise denoising through a stack of layers.
+
+    At denoising step s the query of every sequence is its tracked positions
+    followed by block s (block length `block_len`); the tracked positions come
+    from the previous step's top-k over the importance summed across all layers
+    (none at step 0, fewer than k while few blocks are decoded). Each layer
+    projects and rotates the query, writes its own cache, attends to the whole
+    cache (importance accumulated over layers) and adds its output projection to
+    the hidden states: h <- h + O Wo^T. Each layer's input is RMS-normalised
+    (no learned weight) through a per-token row scale applied inside the
+    projection; without it the residual state of a deep stack with random
+    weights grows without bound. All of it runs through the C ABI.
+    """
+
+    def __init__(self, cfg: StepConfig, device="cuda", layers: Optional[int] = None,
+                 steps: Optional[int] = None):
+        torch = _torch()
+        self.cfg = cfg
+        self.device = device
+        self.n_layers = layers or cfg.layers
+        self.n_steps = steps or cfg.steps
+        self.B, self.H, self.D, self.d = cfg.batch, cfg.n_heads, cfg.head_dim, cfg.d_model
+        self.dtype = dtype_code(cfg.dtype)
+        self.k = cfg.track
+        prompt_len, cache_len, table, num_pages, cu_k = W.multistep_base(cfg)
+        self.prompt_len, self.cache_len, self.table, self.cu_k_np = prompt_len, cache_len, table, cu_k
+        self.T_k = int(cu_k[-1])
+        self.max_pages = int(table.shape[1])
+        self.cu_k = to_device(cu_k, device)
+        self.block_table = to_device(table, device)
+        kc, vc = W.stack_prefill(cfg, num_pages)
+        self.prefill = (kc, vc)
+        dk, dv = to_device(kc, device), to_device(vc, device)
+        self.k_cache = [dk.clone() for _ in range(self.n_layers)]
+        self.v_cache = [dv.clone() for _ in range(self.n_layers)]
+        del dk, dv
+        self.w_qkv, self.w_o = [], []
+        for l in range(self.n_layers):
+            wq, wo = W.layer_weights(cfg, l)
+            self.w_qkv.append(to_device(wq, device))
+            self.w_o.append(to_device(wo, device))
+        # per-step host-side inputs (query lengths, windows, candidates, fresh states)
+        self.steps = []
+        for st in range(self.n_steps):
+            q = W.step_query_lens(cfg, st)
+            cu_q = np.arange(self.B + 1, dtype=np.int32) * q
+            wstart = (prompt_len + cfg.block_len * st).astype(np.int32)
+            cand = W.step_candidates(cfg, st + 1, prompt_len, cu_k)
+            hid = W.step_hidden(cfg, st, int(cu_q[-1]))
+            self.steps.append(dict(Q=q, T_q=int(cu_q[-1]), cu_q=to_device(cu_q, device),
+                                   window_start=to_device(wstart, device),
+                                   cand=to_device(cand, device), hidden=to_device(hid, device)))
+        T_max = max(x["T_q"] for x in self.steps)
+        et = elem_dtype(cfg.dtype)
+        self.h = torch.empty((T_max, self.d), dtype=et, device=device)
+        self.positions = torch.empty(T_max, dtype=torch.int32, device=device)
+        self.q_out = torch.empty((T_max, self.H, self.D), dtype=et, device=device)
+        self.attn_out = torch.empty((T_max, self.H, self.D), dtype=et, device=device)
+        self.importance = torch.empty((self.H, self.T_k), dtype=torch.float32, device=device)
+        self.row_scale = torch.empty(T_max, dtype=torch.float32, device=device)
+        self.topk_pos = torch.full((self.B, self.k), -1, dtype=torch.int32, device=device)
+        self.topk_count = torch.zeros(self.B, dtype=torch.int32, device=device)
+        self.topk_score = torch.empty((self.B, self.k), dtype=torch.float32, device=device)
+        ws = fc.fc_attention_workspace_size(self.B, T_max, self.T_k, self.H, self.D, 1)
+        self.ws_bytes = ws
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        qws = fc.fc_qkv_workspace_size(T_max, self.D, self.dtype)
+        self.qkv_ws_bytes = qws
+        self.qkv_workspace = torch.empty(max(qws, 1), dtype=torch.uint8, device=device)
+        self.scale = 1.0 / math.sqrt(self.D)
+
+    def run_step(self, st: int, stream=None, on_layer=None):
+        cfg = self.cfg
+        x = self.steps[st]
+        T_q = x["T_q"]
+        fc.fc_assemble_query(self.topk_pos if st > 0 else None, self.topk_count if st > 0 else None,
+                             self.k, x["window_start"], x["cu_q"], self.B, self.positions, stream)
+        if stream is not None:
+            with _torch().cuda.stream(stream):
+                self.h[:T_q].copy_(x["hidden"])
+        else:
+            self.h[:T_q].copy_(x["hidden"])
+        for l in range(self.n_layers):
+            fc.fc_rms_row_scale(self.h, T_q, self.d, cfg.rms_eps, self.row_scale, self.dtype, stream)
+            fc.fc_qkv_rope_cache_write(self.h, self.positions, x["cu_q"], self.B, T_q,
+                                       self.w_qkv[l], self.d, self.H, self.D, cfg.rope_base,
+                                       self.k_cache[l], self.v_cache[l], self.block_table,
+                                       self.max_pages, cfg.page_size, self.q_out, None,
+                                       self.qkv_workspace, self.qkv_ws_bytes, self.dtype, stream,
+                                       row_scale=self.row_scale)
+            fc.fc_varlen_bidir_attention(self.q_out, self.k_cache[l], self.v_cache[l],
+                                         self.block_table, self.max_pages, cfg.page_size,
+                                         x["cu_q"], self.cu_k, self.B, x["Q"], self.T_k, self.H,
+                                         self.D, self.scale, self.attn_out, self.importance,
+                                         l > 0, self.workspace, self.ws_bytes, self.dtype, stream)
+            fc.fc_linear_residual(self.attn_out, self.w_o[l], self.h, T_q, self.d, self.d,
+                                  self.dtype, stream)
+            if on_layer is not None:
+                on_layer(st, l)
+        fc.fc_importance_topk(self.importance, self.cu_k, self.B, self.T_k, self.H, x["cand"],
+                              self.k, self.topk_pos, self.topk_count, self.topk_score, stream)

@@ -194,8 +194,10 @@ def multistep_base(cfg: StepConfig, tail_nan: bool = False):
     return prompt_len.astype(np.int32), cache_len.astype(np.int32), table, num_pages, cu_k
 
 
-def layer_cache(cfg: StepConfig, layer: int, num_pages: int):
-    return draw_cache(cfg, num_pages, rng_for(cfg.seed, 300, layer))
+def stack_prefill(cfg: StepConfig, num_pages: int):
+    """Stale-cache prefill of the layer stack: one seeded draw, copied into every
+    layer's cache (each layer's cache then diverges through its own writes)."""
+    return draw_cache(cfg, num_pages, rng_for(cfg.seed, 300))
 
 
 def step_query_lens(cfg: StepConfig, step: int) -> int:
@@ -232,7 +234,8 @@ class VerifyInputs:
     target: np.ndarray          # [sum L^v] planted token (or -1)
 
 
-def make_verify_inputs(cfg: StepConfig, with_logits: bool = True) -> VerifyInputs:
+def make_verify_inputs(cfg: StepConfig, with_logits: bool = True,
+                       with_cache: bool = True) -> VerifyInputs:
     rng = rng_for(cfg.seed, 0)
     B = cfg.batch
     prompt_len, cache_len = draw_lengths(cfg, rng)
@@ -251,7 +254,10 @@ def make_verify_inputs(cfg: StepConfig, with_logits: bool = True) -> VerifyInput
     d = cfg.d_model
     hidden = _normal(rng_for(cfg.seed, 1), (T_q, d), cfg.hidden_std, cfg.dtype)
     w_qkv = _normal(rng_for(cfg.seed, 2), (3 * d, d), cfg.weight_std, cfg.dtype)
-    k_cache, v_cache = draw_cache(cfg, num_pages, rng_for(cfg.seed, 3))
+    if with_cache:
+        k_cache, v_cache = draw_cache(cfg, num_pages, rng_for(cfg.seed, 3))
+    else:
+        k_cache = v_cache = np.zeros((0,), np.uint16)
     step = StepInputs(cfg=cfg, dtype=cfg.dtype, hidden=hidden, positions=positions,
                       cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, w_qkv=w_qkv, k_cache=k_cache,
                       v_cache=v_cache, block_table=table,

@@ -114,8 +114,17 @@ def seq_of_rows(cu_seqlens: np.ndarray) -> np.ndarray:
                           ).astype(np.int64) if cu_seqlens[-1] > 0 else np.zeros(0, np.int64)
 
 
+def rms_normalize(x: np.ndarray, eps: float) -> np.ndarray:
+    """Each row divided by its root mean square: x / sqrt(mean(x^2) + eps) (no
+    learned weight). Used for the inputs of a layer stack, where it keeps the
+    residual state bounded (a reading: the pages list no normalisation)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
 def qkv_rope_cache_write(hidden, positions, cu_seqlens_q, w_qkv, n_heads, head_dim, rope_base,
-                         k_cache, v_cache, block_table, page_size, dtype, write_cache=True):
+                         k_cache, v_cache, block_table, page_size, dtype, write_cache=True,
+                         rms_eps=None):
     """One Flash-Cache projection pass.
 
     Returns a dict with
@@ -126,6 +135,8 @@ def qkv_rope_cache_write(hidden, positions, cu_seqlens_q, w_qkv, n_heads, head_d
       slot_mapping [T_q] int64: page * page_size + offset
     """
     x = as_f64(hidden, dtype)
+    if rms_eps is not None:
+        x = rms_normalize(x, rms_eps)
     w = as_f64(w_qkv, dtype)
     T = x.shape[0]
     H, D = n_heads, head_dim
@@ -323,9 +334,10 @@ def linear_residual(x, w, h, dtype):
 
 def flash_cache_step(hidden, positions, cu_seqlens_q, cu_seqlens_k, w_qkv, n_heads, head_dim,
                      rope_base, k_cache, v_cache, block_table, page_size, cand_mask, k, dtype,
-                     seqs=None, heads=None):
+                     seqs=None, heads=None, rms_eps=None):
     proj = qkv_rope_cache_write(hidden, positions, cu_seqlens_q, w_qkv, n_heads, head_dim,
-                                rope_base, k_cache, v_cache, block_table, page_size, dtype)
+                                rope_base, k_cache, v_cache, block_table, page_size, dtype,
+                                rms_eps=rms_eps)
     scale = 1.0 / math.sqrt(head_dim)
     out, imp = varlen_attention(proj["q_out"], proj["k_cache"], proj["v_cache"], block_table,
                                 page_size, cu_seqlens_q, cu_seqlens_k, scale, heads=heads,

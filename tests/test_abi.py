@@ -61,7 +61,7 @@ def test_qkv_argument_checks():
                 d_model=256, n_heads=2, head_dim=128, rope_base=1e4, k_cache=FAKE, v_cache=FAKE,
                 block_table=FAKE, max_pages_per_seq=4, page_size=16, q_out=FAKE,
                 slot_mapping=None, workspace=FAKE, workspace_bytes=1 << 20,
-                dtype=fc.FC_DTYPE_BF16)
+                dtype=fc.FC_DTYPE_BF16, row_scale=None)
 
     def call(**over):
         a = dict(base)
@@ -147,6 +147,10 @@ def test_topk_verify_linear_assemble_argument_checks():
     with pytest.raises(fc.FlashCacheError) as ei:
         fc.fc_assemble_query(None, FAKE, 4, FAKE, FAKE, 2, FAKE, stream=0)
     assert ei.value.status_name == "FC_ERR_INVALID_VALUE"
+    for args in ((FAKE, 4, 0, 1e-5, FAKE), (FAKE, 4, 16, -1.0, FAKE), (None, 4, 16, 1e-5, FAKE)):
+        with pytest.raises(fc.FlashCacheError) as ei:
+            fc.fc_rms_row_scale(*args, fc.FC_DTYPE_BF16, stream=0)
+        assert ei.value.status_name == "FC_ERR_INVALID_VALUE"
 
 
 def test_last_error_message_names_the_call():

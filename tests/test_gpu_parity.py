@@ -268,7 +268,7 @@ def test_verify_small_vocab(torch_cuda):
     _say("case verify small vocab")
     cfg = dataclasses.replace(CF.C4, name="C4-small", seed=41, batch=5, vocab=1000,
                               verify_len=(3, 20), d_model=256, n_heads=2)
-    vi = W.make_verify_inputs(cfg)
+    vi = W.make_verify_inputs(cfg, with_cache=False)
     vb = VerifyBuffers(vi)
     vb.verify()
     torch.cuda.synchronize()

@@ -422,6 +422,21 @@ def test_verify_two_sequences_row_layout():
 
 
 # ---------------------------------------------------------------------------
+# layer-input RMS normalisation of the layer stack
+# ---------------------------------------------------------------------------
+
+def test_rms_normalize_closed_forms():
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((5, 64)) * rng.uniform(0.1, 30, size=(5, 1))
+    y = O.rms_normalize(x, 0.0)
+    np.testing.assert_allclose(np.sqrt((y * y).mean(1)), 1.0, rtol=1e-14)     # unit RMS rows
+    np.testing.assert_allclose(O.rms_normalize(7.5 * x, 0.0), y, rtol=1e-13)  # scale invariant
+    # a constant row c: c / sqrt(c^2 + eps)
+    c = np.full((1, 10), 3.0)
+    assert abs(O.rms_normalize(c, 1e-5)[0, 0] - 3.0 / math.sqrt(9.0 + 1e-5)) < 1e-15
+
+
+# ---------------------------------------------------------------------------
 # output projection with residual
 # ---------------------------------------------------------------------------
 
