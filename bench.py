@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip the Flash-Verify accept-test component")
     ap.add_argument("--calib", action="store_true",
                     help="run one 256 MiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--cpu-seqs", type=int, default=32,
@@ -92,8 +94,98 @@ def cpu_baseline(inp, n_seqs, budget_s=12.0):
                       f"importance, top-k); {dt:.1f} s"}
 
 
+def verify_component(torch, args):
+    """The Flash-Verify accept test at the verify-shaped workload (B=32, 16..128
+    verified positions per sequence, two views, vocab 126464): logits drawn on the
+    device (values do not change the kernel's work), timed with HIP events."""
+    import numpy as np
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd import flashcache as fc
+    cfg = CF.C4
+    from kv_cache_attention_step_amd import workload as W
+    rng = W.rng_for(cfg.seed, 0)
+    W.draw_lengths(cfg, rng)
+    _, _ = W.draw_paging(cfg, np.full(cfg.batch, cfg.cache_len_fixed), rng)
+    vlen = rng.integers(cfg.verify_len[0], cfg.verify_len[1] + 1, size=cfg.batch)
+    cu_p = torch.tensor(np.concatenate([[0], np.cumsum(vlen)]), dtype=torch.int32, device="cuda:0")
+    n_pos = int(vlen.sum())
+    R = 2 * n_pos
+    gen = torch.Generator(device="cuda:0").manual_seed(cfg.seed)
+    logits = (torch.randn((R, cfg.vocab), generator=gen, device="cuda:0") * cfg.logit_std).to(torch.bfloat16)
+    draft = torch.randint(0, cfg.vocab, (n_pos,), generator=gen, device="cuda:0", dtype=torch.int32)
+    am = torch.empty(R, dtype=torch.int32, device="cuda:0")
+    cf = torch.empty(R, dtype=torch.float32, device="cuda:0")
+    ar = torch.empty(R, dtype=torch.uint8, device="cuda:0")
+    ap = torch.empty(n_pos, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.Stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    ts = []
+    for i in range(args.warmup + args.steps):
+        with torch.cuda.stream(stream):
+            flush.fill_(2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fc.fv_verify_accept(logits, cfg.vocab, cu_p, cfg.batch, R, draft, cfg.tau, am, cf, ar, ap,
+                            stream)
+        e1.record(stream)
+        if i >= args.warmup:
+            ts.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e3
+    nbytes = R * cfg.vocab * 2.0 + R * 9.0 + n_pos * 5.0
+    del logits
+    return {"rows": R, "vocab": cfg.vocab, "avg_us": round(us, 2),
+            "rows_per_s": round(R / (us * 1e-6), 1),
+            "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def stack_main(args):
+    """Layer-stack workload: 32 layers x 32 block-wise denoising steps of one
+    512-token generation (B=32). Prints one JSON line with the time per denoising
+    step (all layers) and per generation."""
+    import numpy as np
+    import torch
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd.runner import LayerStackDriver
+    cfg = CF.C3
+    torch.cuda.set_device(0)
+    drv = LayerStackDriver(cfg, device="cuda:0")
+    stream = torch.cuda.Stream()
+    # warm-up: one full generation (the cache and tracked sets evolve with it)
+    for st in range(cfg.steps):
+        drv.run_step(st, stream)
+    torch.cuda.synchronize()
+    drv = LayerStackDriver(cfg, device="cuda:0")
+    evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in range(cfg.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        drv.run_step(st, stream)
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    q_tokens = sum(x["T_q"] for x in drv.steps)
+    out = {"metric": "layer-stack denoising step time (32 layers, B=32)",
+           "value": round(float(ms.mean()), 4), "unit": "ms/step", "higher_is_better": False,
+           "n_gpus": 1, "steps": cfg.steps, "dtype": cfg.dtype, "data": "synthetic",
+           "config": {"workload": "C3: 32 layers x 32 denoising steps, block 16, track 48, "
+                                  "B=32, caches 768..1536", "layers": cfg.layers},
+           "ms_per_generation": round(float(ms.sum()), 3),
+           "query_tokens_per_s": round(q_tokens * cfg.layers / (ms.sum() * 1e-3), 1),
+           "step_ms_first_last": [round(float(ms[0]), 4), round(float(ms[-1]), 4)],
+           "wall_s": round(wall, 3)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.config == "C3":
+        return stack_main(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
@@ -174,6 +266,7 @@ def main():
     else:
         roof = {"bound": "hbm", "kernel": dominant, "achieved": kd["achieved_gbs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["frac"], "traffic": None}
+    verify = None if args.no_verify else verify_component(torch, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seqs)
@@ -199,6 +292,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "verify_accept_c4": verify,
         "step_ms_min": round(float(step_ms.min()), 4),
         "wall_s_timed_loop": round(wall, 4),
     }
