@@ -134,11 +134,25 @@ FC_DEVICE int acc_row(int mb, int i, int lane) { return mb * 32 + (i >> 2) * 8 +
 FC_DEVICE int acc_col(int nb, int lane) { return nb * 32 + (lane & 31); }
 
 // ---------------------------------------------------------------------------
-// 8-wave variant for large projections: 256 x 256 x 64 tile, 512 threads, two
-// waves per SIMD. Waves form a 2 (rows) x 4 (column groups) grid; each owns 128
-// rows x 64 columns = 4 x 2 accumulator blocks. Global loads run two K-slices
-// ahead of the MFMAs (two register sets, alternated by unrolling the K loop by
-// two), so a slice's load latency is hidden behind two slices of MFMA work.
+// 8-wave variant for large projections: 256 x 256 tile, 512 threads, two waves
+// per SIMD. Waves form a 2 (rows) x 4 (column groups) grid; each owns 128 rows x
+// 64 columns = 4 x 2 accumulator blocks.
+//
+// Operands travel global -> LDS by the buffer unit's direct-to-LDS loads (no
+// staging registers): each K-slice of 32 is one 32 KB stage (A rows, then B
+// rows, 64 bytes each), and four stages rotate through four separate LDS
+// objects, so a slice is requested four slices before it is consumed. Keeping
+// the stages as distinct objects lets the compiler see that a fragment read of
+// one stage does not depend on the loads still landing in another, so it adds
+// no wait of its own; the kernel waits explicitly, per wave, for the one stage
+// that is due (vmcnt) and then meets the other waves at an LDS-only barrier.
+// The barrier sits between the two k-halves of a slice: fragments of half 1 are
+// read before it and those of the next slice's half 0 right after it, each
+// consumed one MFMA cluster later, so LDS latency hides behind MFMAs.
+// A 64-byte row holds four 16-byte chunks; chunk c of row r sits at position
+// c ^ ((r >> 2) & 3), which spreads the 16 rows of a fragment-read phase over
+// all 64 banks. The DMA writes 1 KB (16 rows) per wave instruction in lane
+// order, so the swizzle is applied by choosing which chunk each lane fetches.
 // The column group -> B row map is a template functor so an epilogue can ask
 // for the columns it needs in one lane (e.g. RoPE partners e and e + 64).
 // ---------------------------------------------------------------------------
@@ -154,75 +168,89 @@ struct ColsRopePairs {
   }
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with vmcnt = n and the LDS/export counters left unconstrained
+#define FC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
 template <class COLS>
 struct Gemm8 {
-  static constexpr int BM = 256, BN = 256, BK = 64, THREADS = 512;
+  static constexpr int BM = 256, BN = 256, BK = 32, THREADS = 512;
   static constexpr int MB = 4, NB = 2;
-  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int LD = BM * 8 / THREADS;  // 16-byte chunks per thread per operand
+  static constexpr int HALF = BM * BK * 2;          // one operand of a stage: 16 KB
+  static constexpr int STAGE = 2 * HALF;            // bytes of each of the four LDS stage objects
+  static constexpr int DMA_PER_STAGE = 4;           // direct-to-LDS loads per wave per stage
 
-  struct Regs {
-    u32x4_t a[LD], b[LD];
-  };
+  static FC_DEVICE int off(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
 
-  static FC_DEVICE void load(__amdgpu_buffer_rsrc_t da, int lda, __amdgpu_buffer_rsrc_t db, int ldb,
-                             int m0, int n0, int k0, Regs& r) {
-    const int t = threadIdx.x;
-    const int c = t & 7;
+  // Wave w fills 1 KB blocks w and w + 8 (rows 16 * block ..) of both operands.
+  static FC_DEVICE void dma(char* stage, __amdgpu_buffer_rsrc_t da, int lda, __amdgpu_buffer_rsrc_t db,
+                            int ldb, int m0, int n0, int k0, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      const int row = (t >> 3) + 64 * i;
-      r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(da, ((m0 + row) * lda + k0 + c * 8) * 2, 0, 0);
-      r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(db, ((n0 + row) * ldb + k0 + c * 8) * 2, 0, 0);
+    for (int j = 0; j < 2; ++j) {
+      const int blk = wave + 8 * j;
+      const int row = blk * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(da, (lds_void_t*)(stage + blk * 1024), 16,
+                                               ((m0 + row) * lda + k0 + c * 8) * 2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(db, (lds_void_t*)(stage + HALF + blk * 1024), 16,
+                                               ((n0 + row) * ldb + k0 + c * 8) * 2, 0, 0, 0);
     }
   }
 
-  static FC_DEVICE void store(char* stage, const Regs& r) {
-    const int t = threadIdx.x;
-    const int c = t & 7;
+  static FC_DEVICE void frags(const char* stage, int kk, int wm, int wn, int lane, bf16x8_t (&af)[MB],
+                              bf16x8_t (&bfr)[NB]) {
+    const int lr = lane & 31, c = kk * 2 + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      const int row = (t >> 3) + 64 * i;
-      *(u32x4_t*)(stage + swz_off(row, c)) = r.a[i];
-      *(u32x4_t*)(stage + A_BYTES + swz_off(row, c)) = r.b[i];
-    }
+    for (int mb = 0; mb < MB; ++mb)
+      af[mb] = as_bf16x8(*(const u32x4_t*)(stage + off(wm * 128 + mb * 32 + lr, c)));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      bfr[nb] = as_bf16x8(*(const u32x4_t*)(stage + HALF + off(COLS::col(wn, nb, lr), c)));
   }
 
   // The MFMA cluster runs at raised wave priority: of the two waves sharing a
-  // SIMD, the one feeding the matrix unit wins issue arbitration, which
-  // staggers the pair so one wave's loads and barrier wait overlap the other's
-  // MFMAs.
-  static FC_DEVICE void compute(const char* stage, int wm, int wn, f32x16_t (&acc)[MB][NB]) {
-    const int lane = threadIdx.x & 63;
-    const int lr = lane & 31, hb = lane >> 5;
+  // SIMD, the one feeding the matrix unit wins issue arbitration.
+  static FC_DEVICE void mma(const bf16x8_t (&af)[MB], const bf16x8_t (&bfr)[NB], f32x16_t (&acc)[MB][NB]) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int chunk = kk * 2 + hb;
-      bf16x8_t af[MB], bfr[NB];
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        af[mb] = as_bf16x8(*(const u32x4_t*)(stage + swz_off(wm * 128 + mb * 32 + lr, chunk)));
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        bfr[nb] = as_bf16x8(*(const u32x4_t*)(stage + A_BYTES + swz_off(COLS::col(wn, nb, lr), chunk)));
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32x32x16(af[mb], bfr[nb], acc[mb][nb]);
-    }
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32x32x16(af[mb], bfr[nb], acc[mb][nb]);
     __builtin_amdgcn_s_setprio(0);
   }
 
-  // K must be a multiple of 64. Ends on a barrier. The prefetch loads and LDS
-  // stores are unconditional (slices past K read in-range rows or zeros through
-  // the buffer descriptor and are never consumed): conditional loads make the
-  // compiler's wait counts pessimistic and would serialise the pipeline.
+  // Barrier for LDS hand-over only: the wave's own LDS reads are complete, its
+  // direct-to-LDS loads are covered by the explicit vmcnt wait before it. (A
+  // __syncthreads() would also drain the loads still in flight for later stages.)
+  static FC_DEVICE void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+  // One K-slice t held in `cur` (its half-0 fragments already in a0/b0).
+  // WAIT = loads younger than stage t+1's that may stay in flight; DMA_NEXT
+  // issues stage t+4 into `cur` once every wave is past its reads of it.
+  template <int WAIT, bool DMA_NEXT, bool READ_NEXT>
+  static FC_DEVICE void slice(char* cur, char* next, __amdgpu_buffer_rsrc_t da, int lda,
+                              __amdgpu_buffer_rsrc_t db, int ldb, int m0, int n0, int k_dma, int wave,
+                              int lane, int wm, int wn, bf16x8_t (&a0)[MB], bf16x8_t (&b0)[NB],
+                              bf16x8_t (&a1)[MB], bf16x8_t (&b1)[NB], f32x16_t (&acc)[MB][NB]) {
+    frags(cur, 1, wm, wn, lane, a1, b1);
+    mma(a0, b0, acc);
+    if (READ_NEXT) {
+      FC_WAIT_VMCNT(WAIT);
+      lds_barrier();
+      if (DMA_NEXT) dma(cur, da, lda, db, ldb, m0, n0, k_dma, wave, lane);
+      frags(next, 0, wm, wn, lane, a0, b0);
+    }
+    mma(a1, b1, acc);
+  }
+
+  // K must be a multiple of 128 (four stages). The four stage objects must be
+  // distinct __shared__ arrays of STAGE bytes. Ends with every load landed and
+  // a barrier, so the caller may reuse the stages.
   static FC_DEVICE void run(const uint16_t* __restrict__ A, int lda, int M,
                             const uint16_t* __restrict__ Bm, int ldb, int N, int K, int m0, int n0,
-                            char* lds, f32x16_t (&acc)[MB][NB]) {
+                            char* s0, char* s1, char* s2, char* s3, f32x16_t (&acc)[MB][NB]) {
+    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 2, wn = wave & 3;
 #pragma unroll
@@ -234,22 +262,29 @@ struct Gemm8 {
     const __amdgpu_buffer_rsrc_t da = make_rsrc(A, (uint32_t)M * lda * 2);
     const __amdgpu_buffer_rsrc_t db = make_rsrc(Bm, (uint32_t)N * ldb * 2);
     const int KT = K / BK;
-    Regs x, y;
-    load(da, lda, db, ldb, m0, n0, 0, x);
-    store(lds, x);
-    load(da, lda, db, ldb, m0, n0, BK, x);
-    load(da, lda, db, ldb, m0, n0, 2 * BK, y);
-    __syncthreads();
-    // at slice t (even): stage 0 holds slice t, x holds slice t+1, y slice t+2
-    for (int t = 0; t < KT; t += 2) {
-      compute(lds, wm, wn, acc);
-      store(lds + STAGE, x);
-      __syncthreads();
-      load(da, lda, db, ldb, m0, n0, (t + 3) * BK, x);
-      if (t + 1 < KT) compute(lds + STAGE, wm, wn, acc);
-      store(lds, y);
-      __syncthreads();
-      load(da, lda, db, ldb, m0, n0, (t + 4) * BK, y);
+    constexpr int D = DMA_PER_STAGE;
+    dma(s0, da, lda, db, ldb, m0, n0, 0, wave, lane);
+    dma(s1, da, lda, db, ldb, m0, n0, BK, wave, lane);
+    dma(s2, da, lda, db, ldb, m0, n0, 2 * BK, wave, lane);
+    dma(s3, da, lda, db, ldb, m0, n0, 3 * BK, wave, lane);
+    bf16x8_t a0[MB], b0[NB], a1[MB], b1[NB];
+    FC_WAIT_VMCNT(3 * D);
+    lds_barrier();
+    frags(s0, 0, wm, wn, lane, a0, b0);
+    // steady state: slice t waits for stage t+1 with stages t+2, t+3 in flight
+    // and refills its own stage with slice t+4
+    int t = 0;
+    for (; t < KT - 4; t += 4) {
+      slice<2 * D, true, true>(s0, s1, da, lda, db, ldb, m0, n0, (t + 4) * BK, wave, lane, wm, wn, a0, b0, a1, b1, acc);
+      slice<2 * D, true, true>(s1, s2, da, lda, db, ldb, m0, n0, (t + 5) * BK, wave, lane, wm, wn, a0, b0, a1, b1, acc);
+      slice<2 * D, true, true>(s2, s3, da, lda, db, ldb, m0, n0, (t + 6) * BK, wave, lane, wm, wn, a0, b0, a1, b1, acc);
+      slice<2 * D, true, true>(s3, s0, da, lda, db, ldb, m0, n0, (t + 7) * BK, wave, lane, wm, wn, a0, b0, a1, b1, acc);
     }
+    // last four slices: nothing more to load, fewer loads left to wait past
+    slice<2 * D, false, true>(s0, s1, da, lda, db, ldb, m0, n0, 0, wave, lane, wm, wn, a0, b0, a1, b1, acc);
+    slice<D, false, true>(s1, s2, da, lda, db, ldb, m0, n0, 0, wave, lane, wm, wn, a0, b0, a1, b1, acc);
+    slice<0, false, true>(s2, s3, da, lda, db, ldb, m0, n0, 0, wave, lane, wm, wn, a0, b0, a1, b1, acc);
+    slice<0, false, false>(s3, s0, da, lda, db, ldb, m0, n0, 0, wave, lane, wm, wn, a0, b0, a1, b1, acc);
+    __syncthreads();
   }
 };

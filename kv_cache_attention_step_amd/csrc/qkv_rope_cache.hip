@@ -4,15 +4,16 @@
 // Q and K with RoPE and writes K and V into the cache in a single pass
 // (infernews post "Flash-dLLM 讓擴散式語言模型解碼更快、更省記憶體", paragraph 2).
 //
-// bf16 path: a 256 x 256 x 64 MFMA GEMM tile with 8 waves (gemm_tile.hpp,
-// Gemm8) whose epilogue works on the fp32 accumulators in registers. A wave's
-// 64 columns are half of one head of D = 128 chosen so that the rotate-half
+// bf16 path: a 256 x 256 MFMA GEMM tile with 8 waves (gemm_tile.hpp, Gemm8:
+// operands stream global -> LDS by direct-to-LDS loads, four K-slices ahead)
+// whose epilogue works on the fp32 accumulators in registers. A wave's 64
+// columns are half of one head of D = 128 chosen so that the rotate-half
 // partners e and e + 64 of a token sit in the same lane and register index of
-// its two accumulator blocks: RoPE needs no data exchange. Rotation angles are formed in fp64 as
-// The rotation (cos, sin) per (token, pair) comes from a small table computed
-// first in fp64 (rope_table_kernel), so the angle work is done once per token
-// instead of once per head. Rounded bf16 values go straight to q_out or to the
-// token's cache slot.
+// its two accumulator blocks: RoPE needs no data exchange. The rotation
+// (cos, sin) per (token, pair) comes from a small table computed first in fp64
+// (rope_table_kernel), so the angle work is done once per token instead of once
+// per head. Rounded bf16 values go straight to q_out or to the token's cache
+// slot.
 //
 // f32 path (small models): one work-item per (token, head, rotation pair).
 #include "gemm_tile.hpp"
@@ -55,7 +56,11 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     const float* __restrict__ row_scale, int n_tiles_n) {
   using G = Gemm8<ColsRopePairs>;
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+  // four K-slice stages, kept as distinct objects (see Gemm8)
+  __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[G::STAGE];
 
   // N-tile fastest: consecutive workgroups (spread over the XCDs round-robin)
   // take different weight column blocks, so each XCD streams a disjoint slice of W.
@@ -64,10 +69,10 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
   const int m0 = mt * QKV_BM, n0 = nt * QKV_BN;
 
   f32x16_t acc[G::MB][G::NB];
-  G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, lds, acc);
+  G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, st0, st1, st2, st3, acc);
 
   // token positions and cache slots of this tile's rows
-  int* s_pos = (int*)lds;
+  int* s_pos = (int*)st0;
   int* s_slot = s_pos + QKV_BM;
   const int t = threadIdx.x;
   const int ps_mask = (1 << log2ps) - 1;
