@@ -69,11 +69,6 @@ struct AttnArgs {
 
 FC_DEVICE float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-FC_DEVICE uint32_t pack2(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
-}
 
 // ---- tile loads ----------------------------------------------------------
 // Wave g of the workgroup loads key group g (16 keys) of the tile, K and V.

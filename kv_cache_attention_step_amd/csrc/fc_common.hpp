@@ -33,6 +33,12 @@ FC_DEVICE uint16_t f32_to_bf16(float f) {
 FC_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
+// the same with the hardware pack-convert (round to nearest even, NaN stays NaN)
+FC_DEVICE uint32_t pack2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
 
 // MFMA wrappers: D = A * B + C with A [32 x 16] (lane l: row l%32, k = 8*(l/32)..+7),
 // B [16 x 32] (lane l: column l%32, same k), C/D [32 x 32] (lane l: column l%32,
