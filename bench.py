@@ -25,6 +25,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+# rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch of the C2 step kernels
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c2_step_kernels.pmc_traffic.json")
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
 
@@ -40,6 +42,9 @@ def parse():
                     help="skip the Flash-Verify accept-test component")
     ap.add_argument("--calib", action="store_true",
                     help="run one 256 MiB device copy first (reference for HBM byte counters)")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed steps for this many seconds before the warm-up steps, so "
+                         "that the GPU clocks reach their sustained state")
     ap.add_argument("--cpu-seqs", type=int, default=32,
                     help="sequences of the batch the CPU oracle baseline runs")
     return ap.parse_args()
@@ -120,6 +125,14 @@ def verify_component(torch, args):
     stream = torch.cuda.Stream()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
     ts = []
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s / 2:
+        for _ in range(10):
+            with torch.cuda.stream(stream):
+                flush.fill_(2)
+            fc.fv_verify_accept(logits, cfg.vocab, cu_p, cfg.batch, R, draft, cfg.tau, am, cf, ar,
+                                ap, stream)
+        torch.cuda.synchronize()
     for i in range(args.warmup + args.steps):
         with torch.cuda.stream(stream):
             flush.fill_(2)
@@ -226,6 +239,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # settle: the clocks swing for the first tens of milliseconds of sustained load
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(10):
+            one_step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -257,15 +278,21 @@ def main():
             "achieved_gbs": round(work["topk_bytes"] / (k3_us * 1e-6) / 1e9, 1),
             "frac": round(work["topk_bytes"] / (k3_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    # HBM bytes per launch from the committed counter runs (null once the kernel
+    # sources differ from those the counters were taken on)
+    from kv_cache_attention_step_amd.profiling import load_traffic
+    for name, kd in kernels.items():
+        kd["traffic_bytes"] = load_traffic(TRAFFIC_FILE, name)
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     kd = kernels[dominant]
     if kd["bound"] == "mfma":
         roof = {"bound": "mfma", "kernel": dominant, "achieved": kd["achieved_tflops"],
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kd["frac"],
-                "traffic": None}
+                "traffic": kd["traffic_bytes"]}
     else:
         roof = {"bound": "hbm", "kernel": dominant, "achieved": kd["achieved_gbs"],
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["frac"], "traffic": None}
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["frac"],
+                "traffic": kd["traffic_bytes"]}
     verify = None if args.no_verify else verify_component(torch, args)
     cpu = None
     if not args.no_cpu_baseline:
@@ -293,6 +320,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "verify_accept_c4": verify,
+        "settle": {"seconds": args.settle_s, "steps": settle_steps},
         "step_ms_min": round(float(step_ms.min()), 4),
         "wall_s_timed_loop": round(wall, 4),
     }
