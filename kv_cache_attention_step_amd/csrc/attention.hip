@@ -93,7 +93,10 @@ FC_DEVICE void load_group(const AttnArgs& a, const int32_t* __restrict__ bt, int
     // sequence end so that keys >= L read as 0
     const int nvalid = min(16, L - key0);
     int page = 0;
-    if (nvalid > 0) page = bt[key0 >> a.log2ps];
+    // the block table is read-only for the whole launch: reading it through the
+    // constant address space lets this wave-uniform lookup be a scalar load
+    // instead of a vector load followed by a wait for every vector load in flight
+    if (nvalid > 0) page = ((const __attribute__((address_space(4))) int32_t*)bt)[key0 >> a.log2ps];
     const size_t base = (size_t)page * page_stride + (size_t)h * head_stride + (size_t)(key0 & psm) * AD;
     const uint32_t bytes = nvalid > 0 ? (uint32_t)nvalid * AD * 2 : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc + base, bytes);
