@@ -164,16 +164,11 @@ FC_DEVICE void store_group(char* stage, int g, int lane, const TileRegs& r) {
 
 // ---- MFMA pieces -----------------------------------------------------------
 // S^T block kb (keys kb*32 .. +31 of the tile) for this wave's 32 queries.
-// The MFMA runs are issued at raised wave priority: with two workgroups per CU
-// the wave that is feeding the matrix unit wins issue arbitration over the
-// other wave's softmax arithmetic.
 FC_DEVICE f32x16_t s_block(const char* ks, int kb, const bf16x8_t (&qf)[8], int lane) {
   f32x16_t s = {};
   const char* row = ks + (kb * 32 + (lane & 31)) * K_STRIDE + (lane >> 5) * 16;
-  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) s = mfma32x32x16(as_bf16x8(*(const u32x4_t*)(row + kc * 32)), qf[kc], s);
-  __builtin_amdgcn_s_setprio(0);
   return s;
 }
 
@@ -190,7 +185,6 @@ FC_DEVICE void pv_chunk(const char* vs, int kb, int c, const f32x16_t& p, f32x16
   for (int w = 0; w < 4; ++w) pb[w] = pack2(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
   const bf16x8_t bop = as_bf16x8(pb);
   const int kbase = kb * 32 + c * 16 + (lane >> 5) * 4;
-  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const char* row = vs + (db * 32 + (lane & 31)) * V_STRIDE + kbase * 2;
@@ -200,7 +194,6 @@ FC_DEVICE void pv_chunk(const char* vs, int kb, int c, const f32x16_t& p, f32x16
     av[0] = x0[0]; av[1] = x0[1]; av[2] = x1[0]; av[3] = x1[1];
     o[db] = mfma32x32x16(as_bf16x8(av), bop, o[db]);
   }
-  __builtin_amdgcn_s_setprio(0);
 }
 
 FC_DEVICE void load_q(const AttnArgs& a, int q0, int row, int Q, int h, bf16x8_t (&qf)[8]) {
@@ -368,15 +361,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
       const float mf = fmaxf(m, mo);
       const float lf = (m == -INFINITY ? 0.f : l * fexp2(m - mf)) +
                        (mo == -INFINITY ? 0.f : lo * fexp2(mo - mf));
-      // P = exp2(s c - mf) * (1 / lf); rows past Q get P = 0
-      const float inv_l = row_ok ? 1.f / lf : 0.f;
+      // P = exp2(s c - mf) / lf = exp2(s c - (mf + log2 lf)): the normaliser joins the
+      // exponent's offset, one fma and one exp per score; rows past Q get offset +inf,
+      // so P = 0 (their s is 0: the query row is zero-filled)
+      const float off = row_ok ? mf + __builtin_amdgcn_logf(lf) : INFINITY;
 
       // ---------------- pass 2: P, O += P V, importance ----------------
       load_group<PS_GE16, true>(a, bt, h, 0, L, wave, lane, tr);
       store_group<true>(lds, wave, lane, tr);
       __syncthreads();
       for (int tile = 0; tile < n_tiles; ++tile) {
-        const bool more = tile + 1 < n_tiles;
         load_group<PS_GE16, true>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
         const char* vs = ks + K_TILE;
@@ -385,12 +379,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb) {
           f32x16_t s = s_block(ks, kb, qf, lane);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[i] = fexp2(fmaf(s[i], c, -mf)) * inv_l;
-          if (ragged && !more) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (tile * AKT + s_key(kb, i, lane) >= L) s[i] = 0.f;
-          }
+          for (int i = 0; i < 16; ++i) s[i] = fexp2(fmaf(s[i], c, -off));
+          // no masking needed: keys past L were loaded as zero K and V rows, so their
+          // P multiplies zero V rows and their column sums are never stored
           pv_chunk(vs, kb, 0, s, o, lane);
           pv_chunk(vs, kb, 1, s, o, lane);
           // column sums over this wave's 32 query rows
