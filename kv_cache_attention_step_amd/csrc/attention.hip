@@ -278,7 +278,12 @@ FC_DEVICE float transpose_reduce16(f32x16_t& v, int lane) {
 FC_DEVICE int reduced_key(int kb, int lane) { return s_key(kb, (lane >> 1) & 15, lane); }
 
 // ---- kernels -------------------------------------------------------------------
-template <bool WITH_IMP, bool PS_GE16>
+// KS (key split, for query tiles of at most 64 rows): wave w takes query rows
+// 32 (w & 1) .. +31 and key block w >> 1 (keys 32 (w >> 1) .. +31) of every tile,
+// so all four waves work when a sequence has 64 or fewer queries. The two waves of
+// a query half merge their row statistics after pass 1 and their O partials at the
+// end through LDS; importance sums the two waves that cover a key.
+template <bool WITH_IMP, bool PS_GE16, bool KS>
 __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[A_LDS];
   float* red = (float*)(lds + 2 * A_STAGE);
@@ -309,9 +314,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
     for (int key = t; key < L; key += blockDim.x) a.imp[(size_t)h * a.T_k + k0 + key] = 0.f;
     return;
   }
+  constexpr int ROWS = KS ? 64 : AROWS;        // query rows per row tile
+  const int qh = KS ? (wave & 1) : wave;        // 32-row group of this wave
+  const int kbw = KS ? (wave >> 1) : 0;         // its key block (KS)
   for (int rt = rt_begin; rt < rt_end; ++rt) {
-    if (rt * AROWS >= Q) break;
-    const int row = rt * AROWS + wave * 32 + (lane & 31);
+    if (rt * ROWS >= Q) break;
+    const int row = rt * ROWS + qh * 32 + (lane & 31);
     const bool row_ok = row < Q;
     if (L == 0) {  // no keys: output 0
       const f32x16_t z[4] = {};
@@ -333,34 +341,55 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         const bool more = tile + 1 < n_tiles;
         load_group<PS_GE16, false>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
-        f32x16_t s0 = s_block(ks, 0, qf, lane);
-        f32x16_t s1 = s_block(ks, 1, qf, lane);
+        f32x16_t s0 = s_block(ks, KS ? kbw : 0, qf, lane);
+        f32x16_t s1;
+        if (!KS) s1 = s_block(ks, 1, qf, lane);
         if (ragged && !more) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            if (tile * AKT + s_key(0, i, lane) >= L) s0[i] = -INFINITY;
-            if (tile * AKT + s_key(1, i, lane) >= L) s1[i] = -INFINITY;
+            if (tile * AKT + s_key(KS ? kbw : 0, i, lane) >= L) s0[i] = -INFINITY;
+            if (!KS && tile * AKT + s_key(1, i, lane) >= L) s1[i] = -INFINITY;
           }
         }
         float tmax = s0[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s0[i]);
+        if (!KS) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
+          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
+        }
         const float mn = fmaxf(m, tmax * c);
         const float mref = mn == -INFINITY ? 0.f : mn;   // this lane has seen no key yet
         float sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sum += fexp2(fmaf(s0[i], c, -mref)) + fexp2(fmaf(s1[i], c, -mref));
+        for (int i = 0; i < 16; ++i) sum += fexp2(fmaf(s0[i], c, -mref));
+        if (!KS) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += fexp2(fmaf(s1[i], c, -mref));
+        }
         l = (m == -INFINITY ? 0.f : l * fexp2(m - mn)) + sum;
         m = mn;
         store_group<false>(lds + ((tile + 1) & 1) * A_STAGE, wave, lane, tr);
         __syncthreads();
       }
       const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
-      const float mf = fmaxf(m, mo);
-      const float lf = (m == -INFINITY ? 0.f : l * fexp2(m - mf)) +
-                       (mo == -INFINITY ? 0.f : lo * fexp2(mo - mf));
+      float mf = fmaxf(m, mo);
+      float lf = (m == -INFINITY ? 0.f : l * fexp2(m - mf)) +
+                 (mo == -INFINITY ? 0.f : lo * fexp2(mo - mf));
+      if (KS) {  // merge with the wave that covers the other key block of these rows
+        float* xs = red;   // [wave][32] (m, l); red is free until pass 2's first barrier
+        if (lane < 32) {
+          xs[(wave * 32 + lane) * 2] = mf;
+          xs[(wave * 32 + lane) * 2 + 1] = lf;
+        }
+        __syncthreads();
+        const float mp = xs[((wave ^ 2) * 32 + (lane & 31)) * 2];
+        const float lp = xs[((wave ^ 2) * 32 + (lane & 31)) * 2 + 1];
+        const float mx = fmaxf(mf, mp);
+        lf = (mf == -INFINITY ? 0.f : lf * fexp2(mf - mx)) + (mp == -INFINITY ? 0.f : lp * fexp2(mp - mx));
+        mf = mx;
+        __syncthreads();
+      }
       // P = exp2(s c - mf) / lf = exp2(s c - (mf + log2 lf)): the normaliser joins the
       // exponent's offset, one fma and one exp per score; rows past Q get offset +inf,
       // so P = 0 (their s is 0: the query row is zero-filled)
@@ -376,7 +405,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         const char* vs = ks + K_TILE;
         float* rb = red + (tile & 1) * 4 * AKT;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kk = 0; kk < (KS ? 1 : 2); ++kk) {
+          const int kb = KS ? kbw : kk;
           f32x16_t s = s_block(ks, kb, qf, lane);
 #pragma unroll
           for (int i = 0; i < 16; ++i) s[i] = fexp2(fmaf(s[i], c, -off));
@@ -393,13 +423,32 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         if (t < AKT) {
           const int key = tile * AKT + t;
           if (key < L) {
-            const float v = rb[t] + rb[AKT + t] + rb[2 * AKT + t] + rb[3 * AKT + t];
+            const float v = KS ? rb[(t >> 5) * 2 * AKT + t] + rb[((t >> 5) * 2 + 1) * AKT + t]
+                               : rb[t] + rb[AKT + t] + rb[2 * AKT + t] + rb[3 * AKT + t];
             float* dst = a.imp + (size_t)h * a.T_k + k0 + key;
             *dst = (a.accumulate || rt > 0) ? *dst + v : v;
           }
         }
       }
-      store_o(a, q0, row, Q, h, o, 1.f);
+      if (KS) {  // O = O(key block 0) + O(key block 1), both already normalised
+        float* xo = (float*)lds;   // [2][64 floats x 64 lanes]; stages are free after the loop
+        if (kbw == 1) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xo[(wave - 2) * 4096 + (db * 16 + i) * 64 + lane] = o[db][i];
+        }
+        __syncthreads();
+        if (kbw == 0) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] += xo[wave * 4096 + (db * 16 + i) * 64 + lane];
+          store_o(a, q0, row, Q, h, o, 1.f);
+        }
+      } else {
+        store_o(a, q0, row, Q, h, o, 1.f);
+      }
       __syncthreads();  // LDS reuse by the next row tile
     } else {
       // ---------------- single pass, online softmax ----------------
@@ -412,29 +461,42 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         load_group<PS_GE16, true>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
         const char* vs = ks + K_TILE;
-        f32x16_t s0 = s_block(ks, 0, qf, lane);
-        f32x16_t s1 = s_block(ks, 1, qf, lane);
+        const int kb0 = KS ? kbw : 0;
+        f32x16_t s0 = s_block(ks, kb0, qf, lane);
+        f32x16_t s1;
+        if (!KS) s1 = s_block(ks, 1, qf, lane);
         if (ragged && !more) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            if (tile * AKT + s_key(0, i, lane) >= L) s0[i] = -INFINITY;
-            if (tile * AKT + s_key(1, i, lane) >= L) s1[i] = -INFINITY;
+            if (tile * AKT + s_key(kb0, i, lane) >= L) s0[i] = -INFINITY;
+            if (!KS && tile * AKT + s_key(1, i, lane) >= L) s1[i] = -INFINITY;
           }
         }
         float tmax = s0[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s0[i]);
+        if (!KS) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
+          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
+        }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
-        const float mn = fmaxf(m, tmax);   // finite: key 0 of the first tile is valid
-        const float alpha = fexp2(m - mn); // 0 on the first tile (m = -inf)
+        // without KS key 0 of the first tile is valid, so mn is finite; with KS a key
+        // block can be empty (L <= 32): then mn stays -inf and P = 0
+        const float mn = fmaxf(m, tmax);
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = m == -INFINITY ? 0.f : fexp2(m - mn);  // o = 0 while m = -inf
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          s0[i] = fexp2(fmaf(s0[i], c, -mn));
-          s1[i] = fexp2(fmaf(s1[i], c, -mn));
-          sum += s0[i] + s1[i];
+          s0[i] = fexp2(fmaf(s0[i], c, -mref));
+          sum += s0[i];
+        }
+        if (!KS) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            s1[i] = fexp2(fmaf(s1[i], c, -mref));
+            sum += s1[i];
+          }
         }
         l = l * alpha + sum;
         m = mn;
@@ -444,15 +506,43 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
         }
-        pv_chunk(vs, 0, 0, s0, o, lane);
-        pv_chunk(vs, 0, 1, s0, o, lane);
-        pv_chunk(vs, 1, 0, s1, o, lane);
-        pv_chunk(vs, 1, 1, s1, o, lane);
+        pv_chunk(vs, kb0, 0, s0, o, lane);
+        pv_chunk(vs, kb0, 1, s0, o, lane);
+        if (!KS) {
+          pv_chunk(vs, 1, 0, s1, o, lane);
+          pv_chunk(vs, 1, 1, s1, o, lane);
+        }
         store_group<true>(lds + ((tile + 1) & 1) * A_STAGE, wave, lane, tr);
         __syncthreads();
       }
-      const float lt = l + __shfl_xor(l, 32);
-      store_o(a, q0, row, Q, h, o, 1.f / lt);
+      float lt = l + __shfl_xor(l, 32);
+      if (KS) {  // merge (m, l, O) with the wave of the other key block (split-max merge)
+        float* xo = (float*)lds;   // [2][64 x 64] O partials, then [2][64] (m, l)
+        float* xs = xo + 2 * 4096;
+        if (kbw == 1) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xo[(wave - 2) * 4096 + (db * 16 + i) * 64 + lane] = o[db][i];
+          xs[((wave - 2) * 64 + lane) * 2] = m;
+          xs[((wave - 2) * 64 + lane) * 2 + 1] = lt;
+        }
+        __syncthreads();
+        if (kbw == 0) {
+          const float mp = xs[(wave * 64 + lane) * 2], lp = xs[(wave * 64 + lane) * 2 + 1];
+          const float mx = fmaxf(m, mp);
+          const float fa = m == -INFINITY ? 0.f : fexp2(m - mx);
+          const float fb = mp == -INFINITY ? 0.f : fexp2(mp - mx);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * fa + xo[wave * 4096 + (db * 16 + i) * 64 + lane] * fb;
+          lt = lt * fa + lp * fb;
+          store_o(a, q0, row, Q, h, o, 1.f / lt);
+        }
+      } else {
+        store_o(a, q0, row, Q, h, o, 1.f / lt);
+      }
       __syncthreads();
     }
   }
@@ -611,19 +701,24 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
     a.B = B;
     a.H = n_heads;
     a.T_k = T_k;
-    a.n_rt = (max_seqlen_q + AROWS - 1) / AROWS;
+    // every sequence fits one 64-row tile: split each tile's keys over the waves
+    const bool ks = max_seqlen_q <= 64;
+    a.n_rt = ks ? 1 : (max_seqlen_q + AROWS - 1) / AROWS;
     a.accumulate = accumulate ? 1 : 0;
     a.scale_log2 = softmax_scale * LOG2E;
     hipLaunchKernelGGL(lpt_order, dim3(1), dim3(256), 0, st, cu_seqlens_k, B, (int32_t*)workspace);
     const bool ps16 = page_size >= 16;
     const dim3 grid(importance ? B * n_heads : B * n_heads * a.n_rt);
+#define FC_ATTN_LAUNCH(IMP, PS, KSP) \
+    hipLaunchKernelGGL((attn_bf16_d128<IMP, PS, KSP>), grid, dim3(256), 0, st, a)
     if (importance) {
-      if (ps16) hipLaunchKernelGGL((attn_bf16_d128<true, true>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((attn_bf16_d128<true, false>), grid, dim3(256), 0, st, a);
+      if (ps16) { if (ks) FC_ATTN_LAUNCH(true, true, true); else FC_ATTN_LAUNCH(true, true, false); }
+      else { if (ks) FC_ATTN_LAUNCH(true, false, true); else FC_ATTN_LAUNCH(true, false, false); }
     } else {
-      if (ps16) hipLaunchKernelGGL((attn_bf16_d128<false, true>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((attn_bf16_d128<false, false>), grid, dim3(256), 0, st, a);
+      if (ps16) { if (ks) FC_ATTN_LAUNCH(false, true, true); else FC_ATTN_LAUNCH(false, true, false); }
+      else { if (ks) FC_ATTN_LAUNCH(false, false, true); else FC_ATTN_LAUNCH(false, false, false); }
     }
+#undef FC_ATTN_LAUNCH
     return fc_check_launch("fc_varlen_bidir_attention");
   }
   FC_REQUIRE(head_dim == 64 || head_dim == 128, FC_ERR_UNSUPPORTED,

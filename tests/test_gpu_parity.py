@@ -262,6 +262,58 @@ def test_degenerate_sequences(torch_cuda):
     assert np.all(got["importance"][:, cu_k[1]:cu_k[2]] == 0)
 
 
+def _attention_direct(torch, q_bits, k_cache, v_cache, table, page_size, cu_q, cu_k, H, D,
+                      with_importance, max_seqlen_q):
+    """fc_varlen_bidir_attention on device copies of the inputs."""
+    from kv_cache_attention_step_amd import flashcache as fc
+    dev = "cuda"
+    B = len(cu_q) - 1
+    T_q, T_k = int(cu_q[-1]), int(cu_k[-1])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q = t(q_bits.view(np.int16))
+    kc, vc = t(k_cache.view(np.int16)), t(v_cache.view(np.int16))
+    bt, cq, ck = t(table), t(cu_q), t(cu_k)
+    out = torch.empty((T_q, H, D), dtype=torch.int16, device=dev)
+    imp = torch.full((H, T_k), float("nan"), dtype=torch.float32, device=dev) if with_importance else None
+    wsb = fc.fc_attention_workspace_size(B, T_q, T_k, H, D, with_importance)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    fc.fc_varlen_bidir_attention(q, kc, vc, bt, table.shape[1], page_size, cq, ck, B, max_seqlen_q,
+                                 T_k, H, D, 1.0 / math.sqrt(D), out, imp, 0, ws, wsb, fc.FC_DTYPE_BF16)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint16)
+    return o, (imp.cpu().numpy() if with_importance else None)
+
+
+def test_attention_short_query_tiles(torch_cuda):
+    """Every sequence has at most 64 query rows (the key-split mode: two waves per
+    query half, each on one 32-key block of every tile): a cache shorter than one
+    key block, a block holding a single key, ragged last tiles; with and without
+    importance."""
+    torch = torch_cuda
+    _say("case short query tiles (max_seqlen_q <= 64)")
+    cfg = dataclasses.replace(SMALL_BF16, name="short-q", seed=24)
+    H, D, ps = cfg.n_heads, cfg.head_dim, cfg.page_size
+    rng = W.rng_for(24, 1)
+    L = np.array([5, 33, 200, 650], np.int64)
+    Q = np.array([1, 17, 40, 64], np.int64)
+    cfg = dataclasses.replace(cfg, batch=len(L))
+    table, num_pages = W.draw_paging(cfg, L, rng)
+    k_cache, v_cache = W.draw_cache(cfg, num_pages, rng, cache_len=L, block_table=table,
+                                    tail_nan=True)
+    cu_q = np.concatenate([[0], np.cumsum(Q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    q_bits = W.to_bf16_bits(rng.standard_normal((int(cu_q[-1]), H, D), dtype=np.float32) * 1.3)
+    ref_o, ref_imp = O.varlen_attention(O.bf16_to_f64(q_bits), O.bf16_to_f64(k_cache),
+                                        O.bf16_to_f64(v_cache), table, ps, cu_q, cu_k,
+                                        1.0 / math.sqrt(D))
+    for with_imp in (True, False):
+        o, imp = _attention_direct(torch, q_bits, k_cache, v_cache, table, ps, cu_q, cu_k, H, D,
+                                   with_imp, int(Q.max()))
+        PU.assert_close(O.bf16_to_f64(o), ref_o, "bf16", f"attention out (importance={with_imp})")
+        if with_imp:
+            PU.assert_importance_close(imp, ref_imp)
+
+
 def test_verify_small_vocab(torch_cuda):
     torch = torch_cuda
     from kv_cache_attention_step_amd.runner import VerifyBuffers
