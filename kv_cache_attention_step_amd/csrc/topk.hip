@@ -25,21 +25,36 @@ FC_DEVICE uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int TK_WAVES = TK_THREADS / 64;
+
 // Exclusive prefix over the block of one int per thread; returns the total.
+// Inclusive scan inside each wave by lane shuffles, then one scan of the 16 wave
+// totals: two barriers per call. buf needs TK_WAVES + 1 ints.
 FC_DEVICE int block_exclusive_scan(int v, int* buf, int* out_excl) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < TK_THREADS; off <<= 1) {
-    const int add = t >= off ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  const int incl = buf[t];
-  const int total = buf[TK_THREADS - 1];
+  if (lane == 63) buf[wave] = x;
   __syncthreads();
-  *out_excl = incl - v;
+  if (wave == 0) {
+    const int w = lane < TK_WAVES ? buf[lane] : 0;
+    int wx = w;
+#pragma unroll
+    for (int off = 1; off < TK_WAVES; off <<= 1) {
+      const int y = __shfl_up(wx, off);
+      if (lane >= off) wx += y;
+    }
+    if (lane < TK_WAVES) buf[lane] = wx - w;            // exclusive prefix of the waves
+    if (lane == TK_WAVES - 1) buf[TK_WAVES] = wx;       // block total
+  }
+  __syncthreads();
+  *out_excl = buf[wave] + x - v;
+  const int total = buf[TK_WAVES];
+  __syncthreads();  // buf reused by the next call
   return total;
 }
 
@@ -50,7 +65,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
   __shared__ float s_score[FC_TOPK_MAX_LEN];
   __shared__ uint8_t s_cand[FC_TOPK_MAX_LEN];
   __shared__ int s_hist[256];
-  __shared__ int s_scan[TK_THREADS];
+  __shared__ int s_scan[TK_WAVES + 1];
   __shared__ int s_ctl[4];
 
   const int b = blockIdx.x;
