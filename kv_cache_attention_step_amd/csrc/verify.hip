@@ -5,72 +5,88 @@
 // "Flash-dLLM 讓擴散式語言模型解碼更快、更省記憶體", paragraph 3; threshold 0.9
 // in the README quote of the zhichai.net forum post, section 4).
 //
-// Bandwidth-bound: every logit row (vocab x bf16) is read exactly once. One
-// workgroup per row; each thread streams 16-byte chunks (8 logits), four chunks
-// in flight, keeping a running (max, lowest index of the max, sum of
-// exp(x - max)) that is rescaled only when a chunk raises the max. Partial
-// triples are merged across the wave with shuffles and across waves through LDS
-// (lower index wins ties), so conf = 1 / sum and the argmax are exact up to the
-// fp32 sum. A second tiny kernel ANDs the two views of each position.
+// Bandwidth-bound: every logit row (vocab x bf16) is read once. One workgroup
+// per row; each lane streams 16-byte chunks (8 logits), two chunks in flight,
+// and keeps a running max m, the sum of exp(x - m) over what it has read, and
+// the first chunk group in which m was reached. The per-element work is one
+// fma and one exp2 into the sum; the max is taken once per group and the sum
+// rescaled only when the group raises it. The argmax index is not tracked per
+// element: after the (m, sum) pairs are merged across the block, the few lanes
+// whose m equals the row max re-read their recorded group (at most 32 bytes)
+// and report the lowest index holding it; a block min gives the lowest index
+// of the row. conf = 1 / sum. A second tiny kernel ANDs the two views of each
+// position.
 #include "fc_common.hpp"
 
 #include <math.h>
 
 namespace {
 
-constexpr int VT = 256;
+constexpr int VT = 512;     // threads per row
+constexpr int GROUP = 2;    // 16-byte chunks a lane has in flight
 constexpr float LOG2E_V = 1.4426950408889634f;
 
-struct Run {
-  float m;    // running max, in log2 units (logit * log2 e)
-  int idx;    // lowest index attaining it
-  float s;    // sum of exp2(y - m)
+// Per-lane state. ml = m log2(e) once m is finite and 0 before, so that -inf
+// logits read before the first finite one add 2^-inf = 0. first / cnt locate
+// where m was first reached: chunks first, first + VT, ... (cnt of them), or,
+// with cnt = 0, the element index first itself.
+struct Lane {
+  float m, ml, s;
+  int first, cnt;
 };
 
-FC_DEVICE Run merge(Run a, Run b) {
-  Run r;
-  r.m = fmaxf(a.m, b.m);
-  if (r.m == -INFINITY) {
-    r.s = 0.f;
-    r.idx = min(a.idx, b.idx);
-    return r;
-  }
-  r.s = (a.m == -INFINITY ? 0.f : a.s * exp2f(a.m - r.m)) + (b.m == -INFINITY ? 0.f : b.s * exp2f(b.m - r.m));
-  r.idx = a.m > b.m ? a.idx : (b.m > a.m ? b.idx : min(a.idx, b.idx));
-  return r;
-}
+FC_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-FC_DEVICE void absorb8(Run& r, const u32x4_t& w, int base) {
-  float y[8];
+template <int G>
+FC_DEVICE void absorb(Lane& r, const u32x4_t (&w)[G], int first) {
+  float x[8 * G];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    y[2 * p] = bf16lo_to_f32(w[p]) * LOG2E_V;
-    y[2 * p + 1] = bf16hi_to_f32(w[p]) * LOG2E_V;
-  }
-  float cm = y[0];
-  int ci = 0;
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-  for (int j = 1; j < 8; ++j)
-    if (y[j] > cm) { cm = y[j]; ci = j; }
+    for (int p = 0; p < 4; ++p) {
+      x[8 * g + 2 * p] = bf16lo_to_f32(w[g][p]);
+      x[8 * g + 2 * p + 1] = bf16hi_to_f32(w[g][p]);
+    }
+  float cm = x[0];
+#pragma unroll
+  for (int j = 1; j < 8 * G; ++j) cm = fmaxf(cm, x[j]);
   if (cm > r.m) {
-    r.s = r.m == -INFINITY ? 0.f : r.s * exp2f(r.m - cm);
+    // r.m = -inf leaves s = 0 * 2^-inf = 0
+    r.s *= fast_exp2((r.m - cm) * LOG2E_V);
     r.m = cm;
-    r.idx = base + ci;
+    r.ml = cm * LOG2E_V;
+    r.first = first;
+    r.cnt = G;
   }
-  float add = 0.f;
+  float e[8 * G];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) add += exp2f(y[j] - r.m);
-  r.s += add;
+  for (int j = 0; j < 8 * G; ++j) e[j] = fast_exp2(fmaf(x[j], LOG2E_V, -r.ml));
+#pragma unroll
+  for (int h = 4 * G; h >= 1; h >>= 1)
+#pragma unroll
+    for (int j = 0; j < h; ++j) e[j] += e[j + h];
+  r.s += e[0];
 }
 
-FC_DEVICE void absorb1(Run& r, float x, int v) {
-  const float y = x * LOG2E_V;
-  if (y > r.m) {
-    r.s = r.m == -INFINITY ? 0.f : r.s * exp2f(r.m - y);
-    r.m = y;
-    r.idx = v;
+FC_DEVICE void absorb1(Lane& r, float x, int v) {
+  if (x > r.m) {
+    r.s *= fast_exp2((r.m - x) * LOG2E_V);
+    r.m = x;
+    r.ml = x * LOG2E_V;
+    r.first = v;
+    r.cnt = 0;
   }
-  r.s += exp2f(y - r.m);
+  r.s += fast_exp2(fmaf(x, LOG2E_V, -r.ml));
+}
+
+// (m, s) of two partial sums; s is a sum of exp(x - m)
+FC_DEVICE void merge_ms(float& m, float& s, float om, float os) {
+  const float nm = fmaxf(m, om);
+  if (nm == -INFINITY)
+    s += os;
+  else
+    s = s * exp2f((m - nm) * LOG2E_V) + os * exp2f((om - nm) * LOG2E_V);
+  m = nm;
 }
 
 FC_DEVICE int find_seq_v(const int32_t* __restrict__ cu, int B, int x) {
@@ -92,55 +108,81 @@ __global__ __launch_bounds__(VT) void verify_rows(const uint16_t* __restrict__ l
   __shared__ int s_i[VT / 64];
   const int r = blockIdx.x;
   const int t = threadIdx.x;
+  const int wave = t >> 6;
   const uint16_t* row = logits + (size_t)r * V;
-  Run run{-INFINITY, 0x7FFFFFFF, 0.f};
-  if ((V & 7) == 0) {
-    const int nch = V >> 3;
-    const u32x4_t* src = (const u32x4_t*)row;
+  const u32x4_t* src = (const u32x4_t*)row;
+  const bool vec = (V & 7) == 0;
+  const int nch = V >> 3;
+  Lane run{-INFINITY, 0.f, 0.f, 0, 0};
+  if (vec) {
     int c = t;
-    for (; c + 3 * VT < nch; c += 4 * VT) {
-      const u32x4_t w0 = __builtin_nontemporal_load(src + c);
-      const u32x4_t w1 = __builtin_nontemporal_load(src + c + VT);
-      const u32x4_t w2 = __builtin_nontemporal_load(src + c + 2 * VT);
-      const u32x4_t w3 = __builtin_nontemporal_load(src + c + 3 * VT);
-      absorb8(run, w0, 8 * c);
-      absorb8(run, w1, 8 * (c + VT));
-      absorb8(run, w2, 8 * (c + 2 * VT));
-      absorb8(run, w3, 8 * (c + 3 * VT));
+    for (; c + (GROUP - 1) * VT < nch; c += GROUP * VT) {
+      u32x4_t w[GROUP];
+#pragma unroll
+      for (int g = 0; g < GROUP; ++g) w[g] = __builtin_nontemporal_load(src + c + g * VT);
+      absorb<GROUP>(run, w, c);
     }
-    for (; c < nch; c += VT) absorb8(run, __builtin_nontemporal_load(src + c), 8 * c);
+    for (; c < nch; c += VT) {
+      const u32x4_t w[1] = {__builtin_nontemporal_load(src + c)};
+      absorb<1>(run, w, c);
+    }
   } else {
     for (int v = t; v < V; v += VT) absorb1(run, bf16_to_f32(row[v]), v);
   }
-  // wave merge
+  // row max and sum: wave shuffles, then every thread merges the wave partials
+  float m = run.m, s = run.s;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    Run o;
-    o.m = __shfl_xor(run.m, off);
-    o.s = __shfl_xor(run.s, off);
-    o.idx = __shfl_xor(run.idx, off);
-    run = merge(run, o);
+    const float om = __shfl_xor(m, off), os = __shfl_xor(s, off);
+    merge_ms(m, s, om, os);
   }
-  const int wave = t >> 6;
   if ((t & 63) == 0) {
-    s_m[wave] = run.m;
-    s_s[wave] = run.s;
-    s_i[wave] = run.idx;
+    s_m[wave] = m;
+    s_s[wave] = s;
   }
   __syncthreads();
+  m = s_m[0];
+  s = s_s[0];
+#pragma unroll
+  for (int w = 1; w < VT / 64; ++w) merge_ms(m, s, s_m[w], s_s[w]);
+  // lowest index holding the max: lanes whose own max equals it re-read the
+  // chunks where they first reached it
+  int cand = 0x7FFFFFFF;
+  if (m == -INFINITY) {
+    cand = 0;  // no finite logit: the first index
+  } else if (run.m == m) {
+    if (run.cnt == 0) {
+      cand = run.first;
+    } else {
+      for (int g = 0; g < run.cnt && cand == 0x7FFFFFFF; ++g) {
+        const int ch = run.first + g * VT;
+        const u32x4_t w = src[ch];
+#pragma unroll
+        for (int p = 3; p >= 0; --p) {
+          if (bf16hi_to_f32(w[p]) == m) cand = 8 * ch + 2 * p + 1;
+          if (bf16lo_to_f32(w[p]) == m) cand = 8 * ch + 2 * p;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cand = min(cand, __shfl_xor(cand, off));
+  if ((t & 63) == 0) s_i[wave] = cand;
+  __syncthreads();
   if (t == 0) {
-    Run acc{s_m[0], s_i[0], s_s[0]};
-    for (int w = 1; w < VT / 64; ++w) acc = merge(acc, Run{s_m[w], s_i[w], s_s[w]});
-    const float c = 1.f / acc.s;
+    int idx = s_i[0];
+#pragma unroll
+    for (int w = 1; w < VT / 64; ++w) idx = min(idx, s_i[w]);
+    const float c = 1.f / s;
     // row -> (sequence, view, position): rows of sequence b are [2 p0, 2 p1), so
     // r / 2 lies in [p0, p1)
     const int b = find_seq_v(cu_p, B, r >> 1);
     const int p0 = cu_p[b], n = cu_p[b + 1] - p0;
     const int local = r - 2 * p0;
     const int i = local >= n ? local - n : local;
-    argmax[r] = acc.idx;
+    argmax[r] = idx;
     conf[r] = c;
-    accept_row[r] = (uint8_t)(acc.idx == draft[p0 + i] && c >= tau);
+    accept_row[r] = (uint8_t)(idx == draft[p0 + i] && c >= tau);
   }
 }
 

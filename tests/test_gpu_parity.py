@@ -341,3 +341,80 @@ def test_verify_small_vocab(torch_cuda):
         near_pos = near[2 * p0: 2 * p0 + n] | near[2 * p0 + n: 2 * p0 + 2 * n]
         assert np.array_equal(got["accept_pos"][p0:p1][~near_pos], acc_pos[p0:p1][~near_pos])
     assert acc.sum() > 0 and (acc == 0).sum() > 0   # both outcomes exercised
+
+
+def _verify_direct(torch, logits_bits, cu_p, draft, tau):
+    """fv_verify_accept on device copies of [R, V] bf16 logit bits."""
+    from kv_cache_attention_step_amd import flashcache as fc
+    R, V = logits_bits.shape
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    lg, cp, dr = t(logits_bits.view(np.int16)), t(cu_p.astype(np.int32)), t(draft.astype(np.int32))
+    am = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+    cf = torch.full((R,), float("nan"), dtype=torch.float32, device="cuda")
+    ar = torch.full((R,), 7, dtype=torch.uint8, device="cuda")
+    ap = torch.full((R // 2,), 7, dtype=torch.uint8, device="cuda")
+    fc.fv_verify_accept(lg, V, cp, len(cu_p) - 1, R, dr, tau, am, cf, ar, ap)
+    torch.cuda.synchronize()
+    return am.cpu().numpy(), cf.cpu().numpy(), ar.cpu().numpy(), ap.cpu().numpy()
+
+
+def _edge_rows(rng, V):
+    """16 logit rows (float64, bf16-exact) that stress the argmax and the sum:
+    equal maxima in different lanes, chunks and loop steps, the max at the last
+    element, constant rows, masked (-inf) vocabulary, ramps that raise the max
+    at every step, and peaked rows (confident predictions)."""
+    rnd = lambda: W.bf16_bits_to_f32(W.to_bf16_bits(rng.normal(0.0, 2.0, V))).astype(np.float64)
+    rows = [rnd() for _ in range(16)]
+    top = 30.0
+    rows[1][np.sort(rng.choice(V, size=min(5, V), replace=False))] = top   # scattered ties
+    if V >= 8 * 701:
+        rows[2][8 * 700 + 2] = top      # later chunk of a lower lane ...
+        rows[2][8 * 300 + 5] = top      # ... ties an earlier chunk of a higher lane
+        rows[2][8 * 300 + 7] = top
+    else:
+        rows[2][[V - 1, V // 2, V // 3]] = top
+    rows[3][V - 1] = top                # max only at the last element
+    rows[4][:] = 0.5                    # constant row: argmax 0, conf 1/V
+    rows[5][rng.random(V) < 0.5] = -np.inf
+    rows[5][rng.integers(V)] = 1.0      # keep at least one finite logit
+    rows[6][:] = -np.inf
+    rows[6][V // 2] = -3.0              # one finite logit: conf 1
+    rows[7][[0, V - 1]] = top           # tie between the first and last element
+    ramp = np.linspace(-60.0, 60.0, V)
+    rows[8] = W.bf16_bits_to_f32(W.to_bf16_bits(ramp)).astype(np.float64)
+    rows[9] = rows[8][::-1].copy()
+    for r in (10, 11, 12, 13):
+        rows[r][rng.integers(V)] = 25.0 if r != 13 else 3.0
+    return np.stack(rows)
+
+
+def test_verify_argmax_ties_and_vocab_edges(torch_cuda):
+    """Accept test on hand-shaped rows at several vocab sizes: multiples of 8
+    (16-byte chunk path, fewer chunks than threads at the small sizes), odd
+    sizes (element path), a single logit."""
+    torch = torch_cuda
+    rng = W.rng_for(53, 0)
+    cu_p = np.array([0, 3, 8], np.int32)             # 8 positions, 16 rows
+    tau = 0.9
+    for V in (126464, 4104, 1000, 1003, 8, 7, 1):
+        _say(f"case verify edges vocab={V}")
+        x = _edge_rows(rng, V)
+        bits = W.to_bf16_bits(x)
+        assert np.array_equal(W.bf16_bits_to_f32(bits).astype(np.float64), x)   # bf16-exact
+        am_ref = np.array([int(np.flatnonzero(r == r.max())[0]) for r in x])
+        # drafts: the row's argmax for positions 0..4 (both views), random else
+        draft = rng.integers(0, V, 8).astype(np.int32)
+        for b in range(2):
+            p0, p1 = int(cu_p[b]), int(cu_p[b + 1])
+            n = p1 - p0
+            for i in range(n):
+                if p0 + i < 5:
+                    draft[p0 + i] = am_ref[2 * p0 + i]
+        am, conf, acc, acc_pos = O.verify_accept(bits, cu_p, draft, tau)
+        got = _verify_direct(torch, bits, cu_p, draft, tau)
+        assert np.array_equal(got[0], am), (V, got[0], am)
+        np.testing.assert_allclose(got[1], conf, rtol=2e-6, err_msg=f"conf vocab={V}")
+        near = np.abs(conf - tau) <= 1e-5
+        assert np.array_equal(got[2][~near], acc[~near])
+        if not near.any():
+            assert np.array_equal(got[3], acc_pos)
