@@ -139,20 +139,23 @@ FC_DEVICE int acc_col(int nb, int lane) { return nb * 32 + (lane & 31); }
 // 64 columns = 4 x 2 accumulator blocks.
 //
 // Operands travel global -> LDS by the buffer unit's direct-to-LDS loads (no
-// staging registers): each K-slice of 32 is one 32 KB stage (A rows, then B
-// rows, 64 bytes each), and four stages rotate through four separate LDS
-// objects, so a slice is requested four slices before it is consumed. Keeping
-// the stages as distinct objects lets the compiler see that a fragment read of
-// one stage does not depend on the loads still landing in another, so it adds
-// no wait of its own; the kernel waits explicitly, per wave, for the one stage
-// that is due (vmcnt) and then meets the other waves at an LDS-only barrier.
-// The barrier sits between the two k-halves of a slice: fragments of half 1 are
-// read before it and those of the next slice's half 0 right after it, each
-// consumed one MFMA cluster later, so LDS latency hides behind MFMAs.
-// A 64-byte row holds four 16-byte chunks; chunk c of row r sits at position
-// c ^ ((r >> 2) & 3), which spreads the 16 rows of a fragment-read phase over
-// all 64 banks. The DMA writes 1 KB (16 rows) per wave instruction in lane
-// order, so the swizzle is applied by choosing which chunk each lane fetches.
+// staging registers) in K-slices of 64: a stage is A (256 rows x 128 bytes) then
+// B (256 rows x 128 bytes), 64 KB, and two stages alternate. A load instruction
+// moves 8 rows x 128 bytes, so every group of 8 lanes fetches one whole
+// 128-byte line: L2 serves such a stream at close to twice the rate of 64-byte
+// row pieces. Within a row, 16-byte chunk c sits at position c ^ ((row >> 1) & 7)
+// (chosen by which chunk each lane fetches, since the DMA writes in lane order),
+// so the 16 rows of a fragment-read phase land on distinct bank groups.
+//
+// Schedule ("ping-pong"): waves 0-3 (tile rows 0-127) and waves 4-7 (rows
+// 128-255) put one wave of each group on every SIMD and run half a period apart,
+// separated by s_barrier. In its memory phase a wave reads the fragments of one
+// 32-wide half-slice (both k16 steps) and, on the first half of a slice, issues
+// the next slice into the other stage; in its compute phase it issues the 16
+// MFMAs of that half-slice. So one wave of each SIMD feeds the matrix unit while
+// the other one waits on LDS and memory. A stage is refilled only after both
+// groups have read it (the memory phase ends with lgkmcnt(0) before its barrier)
+// and read only after every wave has waited for its own loads of it.
 // The column group -> B row map is a template functor so an epilogue can ask
 // for the columns it needs in one lane (e.g. RoPE partners e and e + 64).
 // ---------------------------------------------------------------------------
@@ -175,22 +178,21 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <class COLS>
 struct Gemm8 {
-  static constexpr int BM = 256, BN = 256, BK = 32, THREADS = 512;
+  static constexpr int BM = 256, BN = 256, BK = 64, THREADS = 512;
   static constexpr int MB = 4, NB = 2;
-  static constexpr int HALF = BM * BK * 2;          // one operand of a stage: 16 KB
-  static constexpr int STAGE = 2 * HALF;            // bytes of each of the four LDS stage objects
-  static constexpr int DMA_PER_STAGE = 4;           // direct-to-LDS loads per wave per stage
+  static constexpr int HALF = BM * BK * 2;          // one operand of a stage: 32 KB
+  static constexpr int STAGE = 2 * HALF;            // bytes of each of the two LDS stage objects
 
-  static FC_DEVICE int off(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+  static FC_DEVICE int off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
-  // Wave w fills 1 KB blocks w and w + 8 (rows 16 * block ..) of both operands.
+  // Wave w fills 1 KB blocks w, w + 8, w + 16, w + 24 (8 rows each) of both operands.
   static FC_DEVICE void dma(char* stage, __amdgpu_buffer_rsrc_t da, int lda, __amdgpu_buffer_rsrc_t db,
                             int ldb, int m0, int n0, int k0, int wave, int lane) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int blk = wave + 8 * j;
-      const int row = blk * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int row = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(da, (lds_void_t*)(stage + blk * 1024), 16,
                                                ((m0 + row) * lda + k0 + c * 8) * 2, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(db, (lds_void_t*)(stage + HALF + blk * 1024), 16,
@@ -198,6 +200,7 @@ struct Gemm8 {
     }
   }
 
+  // fragments of k16 step kk (0..3) of a stage
   static FC_DEVICE void frags(const char* stage, int kk, int wm, int wn, int lane, bf16x8_t (&af)[MB],
                               bf16x8_t (&bfr)[NB]) {
     const int lr = lane & 31, c = kk * 2 + (lane >> 5);
@@ -209,47 +212,38 @@ struct Gemm8 {
       bfr[nb] = as_bf16x8(*(const u32x4_t*)(stage + HALF + off(COLS::col(wn, nb, lr), c)));
   }
 
-  // The MFMA cluster runs at raised wave priority: of the two waves sharing a
-  // SIMD, the one feeding the matrix unit wins issue arbitration.
   static FC_DEVICE void mma(const bf16x8_t (&af)[MB], const bf16x8_t (&bfr)[NB], f32x16_t (&acc)[MB][NB]) {
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32x32x16(af[mb], bfr[nb], acc[mb][nb]);
-    __builtin_amdgcn_s_setprio(0);
   }
 
-  // Barrier for LDS hand-over only: the wave's own LDS reads are complete, its
-  // direct-to-LDS loads are covered by the explicit vmcnt wait before it. (A
-  // __syncthreads() would also drain the loads still in flight for later stages.)
-  static FC_DEVICE void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-  // One K-slice t held in `cur` (its half-0 fragments already in a0/b0).
-  // WAIT = loads younger than stage t+1's that may stay in flight; DMA_NEXT
-  // issues stage t+4 into `cur` once every wave is past its reads of it.
-  template <int WAIT, bool DMA_NEXT, bool READ_NEXT>
-  static FC_DEVICE void slice(char* cur, char* next, __amdgpu_buffer_rsrc_t da, int lda,
-                              __amdgpu_buffer_rsrc_t db, int ldb, int m0, int n0, int k_dma, int wave,
-                              int lane, int wm, int wn, bf16x8_t (&a0)[MB], bf16x8_t (&b0)[NB],
-                              bf16x8_t (&a1)[MB], bf16x8_t (&b1)[NB], f32x16_t (&acc)[MB][NB]) {
-    frags(cur, 1, wm, wn, lane, a1, b1);
-    mma(a0, b0, acc);
-    if (READ_NEXT) {
-      FC_WAIT_VMCNT(WAIT);
-      lds_barrier();
-      if (DMA_NEXT) dma(cur, da, lda, db, ldb, m0, n0, k_dma, wave, lane);
-      frags(next, 0, wm, wn, lane, a0, b0);
-    }
-    mma(a1, b1, acc);
+  // Phase boundaries; the scheduling barriers keep MFMAs and memory operations
+  // on their own side of them.
+  static FC_DEVICE void bar() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // LDS hand-over: this wave's LDS reads are complete (its direct-to-LDS loads
+  // are covered by an explicit vmcnt wait where needed).
+  static FC_DEVICE void lds_bar() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // K must be a multiple of 128 (four stages). The four stage objects must be
-  // distinct __shared__ arrays of STAGE bytes. Ends with every load landed and
-  // a barrier, so the caller may reuse the stages.
+  // K must be a multiple of 128. st0, st1: two distinct __shared__ arrays of
+  // STAGE bytes (distinct objects, so the compiler sees that fragment reads of
+  // one stage do not depend on loads landing in the other and adds no wait of
+  // its own). Past the last slice the refill goes through a zero-range buffer
+  // descriptor (no memory access), so every slice issues the same loads and the
+  // wait counts are constants. Ends with every load landed and a barrier, so
+  // the caller may reuse the stages.
   static FC_DEVICE void run(const uint16_t* __restrict__ A, int lda, int M,
                             const uint16_t* __restrict__ Bm, int ldb, int N, int K, int m0, int n0,
-                            char* s0, char* s1, char* s2, char* s3, f32x16_t (&acc)[MB][NB]) {
+                            char* st0, char* st1, f32x16_t (&acc)[MB][NB]) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 2, wn = wave & 3;
@@ -261,30 +255,35 @@ struct Gemm8 {
         for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
     const __amdgpu_buffer_rsrc_t da = make_rsrc(A, (uint32_t)M * lda * 2);
     const __amdgpu_buffer_rsrc_t db = make_rsrc(Bm, (uint32_t)N * ldb * 2);
-    const int KT = K / BK;
-    constexpr int D = DMA_PER_STAGE;
-    dma(s0, da, lda, db, ldb, m0, n0, 0, wave, lane);
-    dma(s1, da, lda, db, ldb, m0, n0, BK, wave, lane);
-    dma(s2, da, lda, db, ldb, m0, n0, 2 * BK, wave, lane);
-    dma(s3, da, lda, db, ldb, m0, n0, 3 * BK, wave, lane);
+    const __amdgpu_buffer_rsrc_t dz = make_rsrc(A, 0);
+    const int KS = K / BK;
+    dma(st0, da, lda, db, ldb, m0, n0, 0, wave, lane);
+    FC_WAIT_VMCNT(0);
+    lds_bar();
     bf16x8_t a0[MB], b0[NB], a1[MB], b1[NB];
-    FC_WAIT_VMCNT(3 * D);
-    lds_barrier();
-    frags(s0, 0, wm, wn, lane, a0, b0);
-    // steady state: slice t waits for stage t+1 with stages t+2, t+3 in flight
-    // and refills its own stage with slice t+4
-    int t = 0;
-    for (; t < KT - 4; t += 4) {
-      slice<2 * D, true, true>(s0, s1, da, lda, db, ldb, m0, n0, (t + 4) * BK, wave, lane, wm, wn, a0, b0, a1, b1, acc);
-      slice<2 * D, true, true>(s1, s2, da, lda, db, ldb, m0, n0, (t + 5) * BK, wave, lane, wm, wn, a0, b0, a1, b1, acc);
-      slice<2 * D, true, true>(s2, s3, da, lda, db, ldb, m0, n0, (t + 6) * BK, wave, lane, wm, wn, a0, b0, a1, b1, acc);
-      slice<2 * D, true, true>(s3, s0, da, lda, db, ldb, m0, n0, (t + 7) * BK, wave, lane, wm, wn, a0, b0, a1, b1, acc);
+    if (wm == 1) bar();  // rows 128-255 start half a period later
+    for (int w = 0; w < KS; w += 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // half-slices of slices w (stage 0) and w + 1 (stage 1)
+        char* cur = q < 2 ? st0 : st1;
+        char* oth = q < 2 ? st1 : st0;
+        const int ws = w + (q >> 1);
+        // memory phase
+        if ((q & 1) == 0) {
+          const bool more = ws + 1 < KS;
+          dma(oth, more ? da : dz, lda, more ? db : dz, ldb, m0, n0, (ws + 1) * BK, wave, lane);
+        }
+        frags(cur, 2 * (q & 1), wm, wn, lane, a0, b0);
+        frags(cur, 2 * (q & 1) + 1, wm, wn, lane, a1, b1);
+        if (q & 1) FC_WAIT_VMCNT(0);  // slice ws + 1 landed (for this wave)
+        lds_bar();
+        // compute phase
+        mma(a0, b0, acc);
+        mma(a1, b1, acc);
+        bar();
+      }
     }
-    // last four slices: nothing more to load, fewer loads left to wait past
-    slice<2 * D, false, true>(s0, s1, da, lda, db, ldb, m0, n0, 0, wave, lane, wm, wn, a0, b0, a1, b1, acc);
-    slice<D, false, true>(s1, s2, da, lda, db, ldb, m0, n0, 0, wave, lane, wm, wn, a0, b0, a1, b1, acc);
-    slice<0, false, true>(s2, s3, da, lda, db, ldb, m0, n0, 0, wave, lane, wm, wn, a0, b0, a1, b1, acc);
-    slice<0, false, false>(s3, s0, da, lda, db, ldb, m0, n0, 0, wave, lane, wm, wn, a0, b0, a1, b1, acc);
+    if (wm == 0) bar();
     __syncthreads();
   }
 };

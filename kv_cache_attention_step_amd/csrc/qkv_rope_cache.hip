@@ -5,7 +5,8 @@
 // (infernews post "Flash-dLLM 讓擴散式語言模型解碼更快、更省記憶體", paragraph 2).
 //
 // bf16 path: a 256 x 256 MFMA GEMM tile with 8 waves (gemm_tile.hpp, Gemm8:
-// operands stream global -> LDS by direct-to-LDS loads, four K-slices ahead)
+// operands stream global -> LDS by direct-to-LDS loads in 64-wide K-slices, two
+// wave groups alternating between MFMAs and memory work)
 // whose epilogue works on the fp32 accumulators in registers. A wave's 64
 // columns are half of one head of D = 128 chosen so that the rotate-half
 // partners e and e + 64 of a token sit in the same lane and register index of
@@ -56,11 +57,9 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     const float* __restrict__ row_scale, int n_tiles_n) {
   using G = Gemm8<ColsRopePairs>;
   constexpr int D = 128;
-  // four K-slice stages, kept as distinct objects (see Gemm8)
+  // two K-slice stages, kept as distinct objects (see Gemm8)
   __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st3[G::STAGE];
 
   // N-tile fastest: consecutive workgroups (spread over the XCDs round-robin)
   // take different weight column blocks, so each XCD streams a disjoint slice of W.
@@ -69,7 +68,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
   const int m0 = mt * QKV_BM, n0 = nt * QKV_BN;
 
   f32x16_t acc[G::MB][G::NB];
-  G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, st0, st1, st2, st3, acc);
+  G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, st0, st1, acc);
 
   // token positions and cache slots of this tile's rows
   int* s_pos = (int*)st0;
