@@ -135,8 +135,10 @@ FC_DEVICE int acc_col(int nb, int lane) { return nb * 32 + (lane & 31); }
 
 // ---------------------------------------------------------------------------
 // 8-wave variant for large projections: 256 x 256 tile, 512 threads, two waves
-// per SIMD. Waves form a 2 (rows) x 4 (column groups) grid; each owns 128 rows x
-// 64 columns = 4 x 2 accumulator blocks.
+// per SIMD. Waves form a 4 (rows) x 2 (columns) grid; each owns 64 rows x 128
+// columns = 2 x 4 accumulator blocks, so a wave holds whole 128-wide heads:
+// rotate-half partners e and e + 64 sit in blocks nb and nb + 2 of one lane,
+// and an epilogue can write each row's 256 bytes of a head from one wave.
 //
 // Operands travel global -> LDS by the buffer unit's direct-to-LDS loads (no
 // staging registers) in K-slices of 64: a stage is A (256 rows x 128 bytes) then
@@ -156,30 +158,15 @@ FC_DEVICE int acc_col(int nb, int lane) { return nb * 32 + (lane & 31); }
 // the other one waits on LDS and memory. A stage is refilled only after both
 // groups have read it (the memory phase ends with lgkmcnt(0) before its barrier)
 // and read only after every wave has waited for its own loads of it.
-// The column group -> B row map is a template functor so an epilogue can ask
-// for the columns it needs in one lane (e.g. RoPE partners e and e + 64).
 // ---------------------------------------------------------------------------
-struct ColsLinear {  // wave column group wn, block nb -> tile column
-  static FC_DEVICE int col(int wn, int nb, int lr) { return wn * 64 + nb * 32 + lr; }
-};
-// Column group wn covers half (wn & 1) of head (wn >> 1) of a 128-wide head:
-// block 0 = head columns 32*half + [0, 32), block 1 = 64 + 32*half + [0, 32),
-// so rotate-half partners (e, e + 64) share a lane and a register index.
-struct ColsRopePairs {
-  static FC_DEVICE int col(int wn, int nb, int lr) {
-    return (wn >> 1) * 128 + nb * 64 + (wn & 1) * 32 + lr;
-  }
-};
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // s_waitcnt with vmcnt = n and the LDS/export counters left unconstrained
 #define FC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-template <class COLS>
 struct Gemm8 {
   static constexpr int BM = 256, BN = 256, BK = 64, THREADS = 512;
-  static constexpr int MB = 4, NB = 2;
+  static constexpr int MB = 2, NB = 4;
   static constexpr int HALF = BM * BK * 2;          // one operand of a stage: 32 KB
   static constexpr int STAGE = 2 * HALF;            // bytes of each of the two LDS stage objects
 
@@ -206,10 +193,10 @@ struct Gemm8 {
     const int lr = lane & 31, c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      af[mb] = as_bf16x8(*(const u32x4_t*)(stage + off(wm * 128 + mb * 32 + lr, c)));
+      af[mb] = as_bf16x8(*(const u32x4_t*)(stage + off(wm * 64 + mb * 32 + lr, c)));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      bfr[nb] = as_bf16x8(*(const u32x4_t*)(stage + HALF + off(COLS::col(wn, nb, lr), c)));
+      bfr[nb] = as_bf16x8(*(const u32x4_t*)(stage + HALF + off(wn * 128 + nb * 32 + lr, c)));
   }
 
   static FC_DEVICE void mma(const bf16x8_t (&af)[MB], const bf16x8_t (&bfr)[NB], f32x16_t (&acc)[MB][NB]) {
@@ -246,7 +233,7 @@ struct Gemm8 {
                             char* st0, char* st1, f32x16_t (&acc)[MB][NB]) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -261,7 +248,7 @@ struct Gemm8 {
     FC_WAIT_VMCNT(0);
     lds_bar();
     bf16x8_t a0[MB], b0[NB], a1[MB], b1[NB];
-    if (wm == 1) bar();  // rows 128-255 start half a period later
+    if (wm >= 2) bar();  // rows 128-255 start half a period later
     for (int w = 0; w < KS; w += 2) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {  // half-slices of slices w (stage 0) and w + 1 (stage 1)
@@ -283,7 +270,7 @@ struct Gemm8 {
         bar();
       }
     }
-    if (wm == 0) bar();
+    if (wm < 2) bar();
     __syncthreads();
   }
 };

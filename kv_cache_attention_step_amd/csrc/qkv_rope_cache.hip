@@ -6,15 +6,15 @@
 //
 // bf16 path: a 256 x 256 MFMA GEMM tile with 8 waves (gemm_tile.hpp, Gemm8:
 // operands stream global -> LDS by direct-to-LDS loads in 64-wide K-slices, two
-// wave groups alternating between MFMAs and memory work)
-// whose epilogue works on the fp32 accumulators in registers. A wave's 64
-// columns are half of one head of D = 128 chosen so that the rotate-half
-// partners e and e + 64 of a token sit in the same lane and register index of
-// its two accumulator blocks: RoPE needs no data exchange. The rotation
-// (cos, sin) per (token, pair) comes from a small table computed first in fp64
-// (rope_table_kernel), so the angle work is done once per token instead of once
-// per head. Rounded bf16 values go straight to q_out or to the token's cache
-// slot.
+// wave groups alternating between MFMAs and memory work) whose epilogue works
+// on the fp32 accumulators in registers. Each wave holds 64 rows of one whole
+// head of D = 128, with the rotate-half partners e and e + 64 of a token in
+// the same lane and register index of two accumulator blocks: RoPE needs no
+// data exchange. The rotation (cos, sin) per (token, pair) comes from a small
+// table computed first in fp64 (rope_table_kernel), so the angle work is done
+// once per token instead of once per head. Rounded bf16 values pass through a
+// wave-private LDS tile so that they leave as 16-byte row chunks, whole
+// 128-byte lines, to q_out or to the token's cache slot.
 //
 // f32 path (small models): one work-item per (token, head, rotation pair).
 #include "gemm_tile.hpp"
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     const int32_t* __restrict__ block_table, int maxp, int log2ps, uint16_t* __restrict__ q_out,
     int32_t* __restrict__ slot_mapping, const float2* __restrict__ rope,
     const float* __restrict__ row_scale, int n_tiles_n) {
-  using G = Gemm8<ColsRopePairs>;
+  using G = Gemm8;
   constexpr int D = 128;
   // two K-slice stages, kept as distinct objects (see Gemm8)
   __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
@@ -94,53 +94,67 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
 
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63, lr = lane & 31;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int col0 = n0 + (wn >> 1) * D;      // first column of this wave's head
+  const int wm = wave >> 1, wn = wave & 1;
+  const int col0 = n0 + wn * D;             // first column of this wave's head
   const int region = col0 / d;              // 0 = Q, 1 = K, 2 = V
   const int h = (col0 - region * d) / D;
-  const int e = (wn & 1) * 32 + lr;         // rotation pair (e, e + 64) of this lane
 
-  if (row_scale) {  // per-token input normalisation: (x r) W^T = r (x W^T)
-#pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float r = row_scale[min(m0 + wm * 128 + acc_row(mb, i, lane), M - 1)];
-        acc[mb][0][i] *= r;
-        acc[mb][1][i] *= r;
-      }
-  }
-  if (region < 2) {
-#pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = min(m0 + wm * 128 + acc_row(mb, i, lane), M - 1);
-        const float2 cs = rope[(size_t)row * (D / 2) + e];
-        const float x = acc[mb][0][i], y = acc[mb][1][i];
-        acc[mb][0][i] = x * cs.x - y * cs.y;
-        acc[mb][1][i] = y * cs.x + x * cs.y;
-      }
-  }
-
+  // Per 32-row block: row scale and RoPE in registers, bf16 values into a
+  // wave-private 8 KB LDS tile (32 rows of 256 bytes; rows with bit 2 set swap
+  // their 64-byte halves, so the two row groups of a write phase fall on
+  // different banks), then 16-byte row chunks out, 16 lanes per row: every
+  // store writes whole 128-byte lines. Q and K are rotated, V is not.
+  char* tile = st1 + wave * (32 * 256);
   uint16_t* cache = region == 1 ? kc : vc;
+  const bool rot = region < 2;
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb)
+  for (int mb = 0; mb < G::MB; ++mb) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int rl = wm * 128 + acc_row(mb, i, lane);
-      const int row = m0 + rl;
-      if (row >= M) continue;
-      uint16_t* dst;
-      if (region == 0) {
-        dst = q_out + ((size_t)row * H + h) * D;
-      } else {
-        const int slot = s_slot[rl];
-        dst = cache + (((size_t)(slot >> log2ps) * H + h) * (ps_mask + 1) + (slot & ps_mask)) * D;
+      const int row = min(m0 + wm * 64 + acc_row(mb, i, lane), M - 1);
+      const float r = row_scale ? row_scale[row] : 1.f;  // (x r) W^T = r (x W^T)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        // rotate-half partners e and e + 64 are blocks nb and nb + 2 of the same lane
+        const float2 cs = rope[(size_t)row * (D / 2) + nb * 32 + lr];
+        const float x = acc[mb][nb][i] * r, y = acc[mb][nb + 2][i] * r;
+        acc[mb][nb][i] = rot ? x * cs.x - y * cs.y : x;
+        acc[mb][nb + 2][i] = rot ? y * cs.x + x * cs.y : y;
       }
-      dst[e] = f32_to_bf16(acc[mb][0][i]);
-      dst[e + 64] = f32_to_bf16(acc[mb][1][i]);
     }
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const int rr = acc_row(0, i, lane);  // rows rr and rr + 1 of the block (same bit 2)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) {
+        const uint32_t p = pack2(acc[mb][nb][i], acc[mb][nb][i + 1]);
+        const int b = ((nb * 32 + lr) * 2) ^ (((rr >> 2) & 1) << 6);
+        *(uint16_t*)(tile + rr * 256 + b) = (uint16_t)p;
+        *(uint16_t*)(tile + (rr + 1) * 256 + b) = (uint16_t)(p >> 16);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's tile writes are done
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = lane + 64 * j;
+      const int rr = q >> 4, c = q & 15;
+      const u32x4_t v = *(const u32x4_t*)(tile + rr * 256 + ((c * 16) ^ (((rr >> 2) & 1) << 6)));
+      const int rl = wm * 64 + mb * 32 + rr;
+      const int row = m0 + rl;
+      if (row < M) {
+        uint16_t* dst;
+        if (region == 0) {
+          dst = q_out + ((size_t)row * H + h) * D;
+        } else {
+          const int slot = s_slot[rl];
+          dst = cache + (((size_t)(slot >> log2ps) * H + h) * (ps_mask + 1) + (slot & ps_mask)) * D;
+        }
+        *(u32x4_t*)(dst + c * 8) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // tile reads done before the next block's writes
+  }
 }
 
 // fp32: block = (token, region*H + head), D/2 threads, thread e computes the
