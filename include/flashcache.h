@@ -113,7 +113,9 @@ const char* fc_version(void);
  *               per-token rotation table; overwritten; NULL allowed when that
  *               size is 0; calls that overlap on one workspace race)
  * Supported: bf16 with D = 128 and d a multiple of 256; f32 with D in {64,128}.
- * page_size must be a power of two in [1, 256].
+ * page_size must be a power of two in [1, 256]. bf16: hidden, w_qkv, q_out,
+ * k_cache, v_cache and workspace must be 16-byte aligned (FC_ERR_INVALID_VALUE
+ * otherwise).
  */
 fc_status_t fc_qkv_rope_cache_write(
     const void* hidden, const int32_t* positions, const int32_t* cu_seqlens_q, int32_t B,

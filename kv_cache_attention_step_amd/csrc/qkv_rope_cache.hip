@@ -34,18 +34,21 @@ FC_DEVICE int find_seq(const int32_t* __restrict__ cu, int B, int row) {
   return lo;
 }
 
-// Rotation table: rope[t][e] = (cos, sin) of positions[t] * base^(-2e/D), in
-// fp64 then rounded to fp32. One entry per (token, pair); every Q and K head
-// of the token reuses it.
+// Rotation table: (cos, sin) of positions[t] * base^(-2e/D) for pair e of
+// token t, in fp64 then rounded to fp32. One entry per (token, pair); every Q
+// and K head of the token reuses it. Within a token, pairs e and e + half/2
+// are adjacent (entry 2 (e mod half/2) + e div half/2), so the lane that
+// rotates both loads them with one 16-byte load.
 __global__ void rope_table_kernel(const int32_t* __restrict__ positions, int T, int half,
                                   float rope_base, float2* __restrict__ table) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * half) return;
   const int t = idx / half, e = idx - t * half;
+  const int q = half / 2;
   const double inv_freq = exp2(-(double)e / (double)half * log2((double)rope_base));
   double sn, cs;
   sincos((double)positions[t] * inv_freq, &sn, &cs);
-  table[idx] = make_float2((float)cs, (float)sn);
+  table[(size_t)t * half + 2 * (e % q) + e / q] = make_float2((float)cs, (float)sn);
 }
 
 __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
@@ -114,10 +117,12 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     for (int i = 0; i < 16; ++i) {
       const int row = min(m0 + wm * 64 + acc_row(mb, i, lane), M - 1);
       const float r = row_scale ? row_scale[row] : 1.f;  // (x r) W^T = r (x W^T)
+      // (cos, sin) of pairs lr and lr + 32
+      const float4 cs2 = *(const float4*)(rope + (size_t)row * (D / 2) + 2 * lr);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         // rotate-half partners e and e + 64 are blocks nb and nb + 2 of the same lane
-        const float2 cs = rope[(size_t)row * (D / 2) + nb * 32 + lr];
+        const float2 cs = nb == 0 ? make_float2(cs2.x, cs2.y) : make_float2(cs2.z, cs2.w);
         const float x = acc[mb][nb][i] * r, y = acc[mb][nb + 2][i] * r;
         acc[mb][nb][i] = rot ? x * cs.x - y * cs.y : x;
         acc[mb][nb + 2][i] = rot ? y * cs.x + x * cs.y : y;
@@ -302,6 +307,11 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
     FC_REQUIRE(workspace && workspace_bytes >= fc_qkv_workspace_size(T_q, head_dim, dtype),
                FC_ERR_WORKSPACE, "fc_qkv_rope_cache_write: workspace of %zu bytes required",
                fc_qkv_workspace_size(T_q, head_dim, dtype));
+    // 16-byte loads and stores of rows
+    const uintptr_t mis = (uintptr_t)hidden | (uintptr_t)w_qkv | (uintptr_t)q_out |
+                          (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)workspace;
+    FC_REQUIRE((mis & 15) == 0, FC_ERR_INVALID_VALUE,
+               "fc_qkv_rope_cache_write: bf16 device pointers must be 16-byte aligned");
     const int n_tiles_n = (write_cache ? 3 * d_model : d_model) / QKV_BN;
     const int n_tiles_m = (T_q + QKV_BM - 1) / QKV_BM;
     const int n_rot = T_q * (head_dim / 2);

@@ -88,6 +88,11 @@ def test_qkv_argument_checks():
     assert need >= 4 * 64 * 8
     expect("FC_ERR_WORKSPACE", workspace_bytes=need - 1)
     expect("FC_ERR_WORKSPACE", workspace=None)
+    for name in ("hidden", "w_qkv", "q_out", "k_cache", "workspace"):   # 16-byte rows
+        over = {name: FAKE + 8}
+        if name == "k_cache":
+            over["v_cache"] = FAKE + 8
+        expect("FC_ERR_INVALID_VALUE", **over)
     assert fc.fc_qkv_workspace_size(4, 64, fc.FC_DTYPE_F32) == 0
     # nothing to do is not an error
     call(T_q=0)(0)
