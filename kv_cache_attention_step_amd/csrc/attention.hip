@@ -12,9 +12,11 @@
 // (sequence, head) and up to 128 query rows (32 per wave), so every K/V byte of
 // that head is fetched from HBM once and shared by all query rows through LDS.
 // Per 64-key tile:
-//   * K tile [64 keys][128] and V tile, transposed to V^T [128][64], are staged in
-//     LDS (double buffered; the next tile's global loads are in flight while the
-//     current one is consumed).
+//   * K tile [64 keys][128] and V tile [64 keys][128] are staged key-major in LDS
+//     (double buffered; the next tile's global loads are in flight while the
+//     current one is consumed). The V^T operand of the PV product is read with
+//     gfx950's transposing LDS read (ds_read_b64_tr_b16), so V needs no transpose
+//     on its way in.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the accumulator of a 32x32
 //     block gives each lane one query (lane % 32) and 16 keys, so row statistics
 //     need only one cross-half exchange, and the probabilities are already in the
@@ -40,9 +42,9 @@ constexpr int AD = 128;                 // head dim
 constexpr int AKT = 64;                 // keys per tile (4 groups of 16, one per wave)
 constexpr int AROWS = 128;              // query rows per workgroup pass
 constexpr int K_STRIDE = AD * 2 + 16;   // bytes per key row of the K tile
-constexpr int V_STRIDE = AKT * 2 + 8;   // bytes per dim row of the V^T tile
+constexpr int V_STRIDE = AD * 2;        // bytes per key row of the V tile
 constexpr int K_TILE = AKT * K_STRIDE;
-constexpr int V_TILE = AD * V_STRIDE;
+constexpr int V_TILE = AKT * V_STRIDE;
 constexpr int A_STAGE = K_TILE + V_TILE;
 constexpr int A_RED = 2 * 4 * AKT * 4;  // double-buffered [wave][key] fp32 partial sums
 constexpr int A_LDS = 2 * A_STAGE + A_RED;
@@ -75,7 +77,7 @@ FC_DEVICE float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Loads past the last tile are harmless (zero-length descriptor or key check)
 // and are issued unconditionally so the compiler's wait counts stay exact.
 // K: lane l loads 16-byte chunk (l & 15) of keys (l >> 4) + 4 i.
-// V: lane l loads dims 8 (l >> 2) .. +7 of keys 4 (l & 3) .. +3 (transposed on store).
+// V: the same pattern as K.
 struct TileRegs {
   u32x4_t k[4];
   u32x4_t v[4];
@@ -107,7 +109,7 @@ FC_DEVICE void load_group(const AttnArgs& a, const int32_t* __restrict__ bt, int
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vc + base, bytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (4 * (lane & 3) + i) * (AD * 2) + (lane >> 2) * 16, 0, KV_POLICY);
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((lane >> 4) + 4 * i) * (AD * 2) + (lane & 15) * 16, 0, KV_POLICY);
     }
   } else {
 #pragma unroll
@@ -124,10 +126,10 @@ FC_DEVICE void load_group(const AttnArgs& a, const int32_t* __restrict__ bt, int
     if (WANT_V) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = key0 + 4 * (lane & 3) + i;
+        const int key = key0 + (lane >> 4) + 4 * i;
         if (key < L) {
           const size_t off = (size_t)bt[key >> a.log2ps] * page_stride + (size_t)h * head_stride +
-                             (size_t)(key & psm) * AD + (lane >> 2) * 8;
+                             (size_t)(key & psm) * AD + (lane & 15) * 8;
           r.v[i] = __builtin_nontemporal_load((const u32x4_t*)(a.vc + off));
         } else {
           r.v[i] = u32x4_t{0, 0, 0, 0};
@@ -144,20 +146,12 @@ FC_DEVICE void store_group(char* stage, int g, int lane, const TileRegs& r) {
   for (int i = 0; i < 4; ++i)
     *(u32x4_t*)(ks + (g * 16 + (lane >> 4) + 4 * i) * K_STRIDE + (lane & 15) * 16) = r.k[i];
   if (WANT_V) {
+    // key-major V rows; 16-byte chunk c of key row k sits at position c ^ 4 (k & 3)
     char* vs = stage + K_TILE;
-    const int key0 = g * 16 + 4 * (lane & 3);
-    const int d0 = 8 * (lane >> 2);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      // r.v[j][p] holds dim d0 + 2p (low half) and d0 + 2p + 1 (high half) of key j
-      const uint32_t w0 = r.v[0][p], w1 = r.v[1][p], w2 = r.v[2][p], w3 = r.v[3][p];
-      u32x2_t lo, hi;
-      lo[0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-      *(u32x2_t*)(vs + (d0 + 2 * p) * V_STRIDE + key0 * 2) = lo;
-      *(u32x2_t*)(vs + (d0 + 2 * p + 1) * V_STRIDE + key0 * 2) = hi;
+    for (int i = 0; i < 4; ++i) {
+      const int key = g * 16 + (lane >> 4) + 4 * i;
+      *(u32x4_t*)(vs + key * V_STRIDE + (((lane & 15) ^ (4 * (key & 3))) * 16)) = r.v[i];
     }
   }
 }
@@ -184,14 +178,28 @@ FC_DEVICE void pv_chunk(const char* vs, int kb, int c, const f32x16_t& p, f32x16
 #pragma unroll
   for (int w = 0; w < 4; ++w) pb[w] = pack2(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
   const bf16x8_t bop = as_bf16x8(pb);
-  const int kbase = kb * 32 + c * 16 + (lane >> 5) * 4;
+  // V^T operand by transposing reads of the key-major tile: within each 16-lane
+  // group, source lane a names 4 dims of key kbase + a/4, and lane i receives dim
+  // d0 + i of keys kbase .. kbase + 3
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  const int a = lane & 15;
+  const int key_lo = kb * 32 + c * 16 + (lane >> 5) * 4 + (a >> 2);   // k index j = 0..3
+  const int key_hi = key_lo + 8;                                         // j = 4..7
+  const char* rlo = vs + key_lo * V_STRIDE;
+  const char* rhi = vs + key_hi * V_STRIDE;
+  const int sw = 8 * (a >> 2);   // (key & 3) * 8 units of 8 bytes
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const char* row = vs + (db * 32 + (lane & 31)) * V_STRIDE + kbase * 2;
+    const int u = 8 * db + 4 * ((lane >> 4) & 1) + (a & 3);   // 8-byte unit: dims 4u .. 4u+3
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(rlo + ((u ^ sw) * 8)));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(rhi + ((u ^ sw) * 8)));
     u32x4_t av;
-    const u32x2_t x0 = *(const u32x2_t*)row;
-    const u32x2_t x1 = *(const u32x2_t*)(row + 16);
-    av[0] = x0[0]; av[1] = x0[1]; av[2] = x1[0]; av[3] = x1[1];
+    av[0] = __builtin_bit_cast(u32x2_t, lo)[0];
+    av[1] = __builtin_bit_cast(u32x2_t, lo)[1];
+    av[2] = __builtin_bit_cast(u32x2_t, hi)[0];
+    av[3] = __builtin_bit_cast(u32x2_t, hi)[1];
     o[db] = mfma32x32x16(as_bf16x8(av), bop, o[db]);
   }
 }
