@@ -54,6 +54,12 @@ FC_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 FC_DEVICE bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// LDS pointer type of the direct-to-LDS buffer loads
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with vmcnt = n and the LDS/export counters left unconstrained
+#define FC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
 // ---------------------------------------------------------------------------
 // host-side error plumbing (fc_status.cpp)
 // ---------------------------------------------------------------------------

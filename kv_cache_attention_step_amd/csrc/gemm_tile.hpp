@@ -134,23 +134,26 @@ FC_DEVICE int acc_row(int mb, int i, int lane) { return mb * 32 + (i >> 2) * 8 +
 FC_DEVICE int acc_col(int nb, int lane) { return nb * 32 + (lane & 31); }
 
 // ---------------------------------------------------------------------------
-// 8-wave variant for large projections: 256 x 256 tile, 512 threads, two waves
-// per SIMD. Waves form a 4 (rows) x 2 (columns) grid; each owns 64 rows x 128
-// columns = 2 x 4 accumulator blocks, so a wave holds whole 128-wide heads:
-// rotate-half partners e and e + 64 sit in blocks nb and nb + 2 of one lane,
-// and an epilogue can write each row's 256 bytes of a head from one wave.
+// 8-wave variant for large projections: BM x 256 tile (BM = 256 or 128), 512
+// threads, two waves per SIMD. Waves form a 4 (rows) x 2 (columns) grid; each
+// owns BM/4 rows x 128 columns = (BM/128) x 4 accumulator blocks, so a wave holds
+// whole 128-wide heads: rotate-half partners e and e + 64 sit in blocks nb and
+// nb + 2 of one lane, and an epilogue can write each row's 256 bytes of a head
+// from one wave. The 128-row tile doubles the tile count where 256-row tiles
+// would leave most of a last round of workgroups empty (M = 2048: 768 tiles
+// instead of 384 over 256 CUs).
 //
 // Operands travel global -> LDS by the buffer unit's direct-to-LDS loads (no
-// staging registers) in K-slices of 64: a stage is A (256 rows x 128 bytes) then
-// B (256 rows x 128 bytes), 64 KB, and two stages alternate. A load instruction
+// staging registers) in K-slices of 64: a stage is A (BM rows x 128 bytes) then
+// B (256 rows x 128 bytes), 64 or 48 KB, and two stages alternate. A load instruction
 // moves 8 rows x 128 bytes, so every group of 8 lanes fetches one whole
 // 128-byte line: L2 serves such a stream at close to twice the rate of 64-byte
 // row pieces. Within a row, 16-byte chunk c sits at position c ^ ((row >> 1) & 7)
 // (chosen by which chunk each lane fetches, since the DMA writes in lane order),
 // so the 16 rows of a fragment-read phase land on distinct bank groups.
 //
-// Schedule ("ping-pong"): waves 0-3 (tile rows 0-127) and waves 4-7 (rows
-// 128-255) put one wave of each group on every SIMD and run half a period apart,
+// Schedule ("ping-pong"): waves 0-3 (the first half of the tile rows) and waves
+// 4-7 (the second half) put one wave of each group on every SIMD and run half a period apart,
 // separated by s_barrier. In its memory phase a wave reads the fragments of one
 // 32-wide half-slice (both k16 steps) and, on the first half of a slice, issues
 // the next slice into the other stage; in its compute phase it issues the 16
@@ -159,20 +162,20 @@ FC_DEVICE int acc_col(int nb, int lane) { return nb * 32 + (lane & 31); }
 // groups have read it (the memory phase ends with lgkmcnt(0) before its barrier)
 // and read only after every wave has waited for its own loads of it.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt with vmcnt = n and the LDS/export counters left unconstrained
-#define FC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
+template <int BM_>
 struct Gemm8 {
-  static constexpr int BM = 256, BN = 256, BK = 64, THREADS = 512;
-  static constexpr int MB = 2, NB = 4;
-  static constexpr int HALF = BM * BK * 2;          // one operand of a stage: 32 KB
-  static constexpr int STAGE = 2 * HALF;            // bytes of each of the two LDS stage objects
+  static constexpr int BM = BM_, BN = 256, BK = 64, THREADS = 512;
+  static constexpr int MB = BM / 128, NB = 4;
+  static constexpr int WROWS = BM / 4;              // tile rows of one wave
+  static constexpr int HALF_A = BM * BK * 2;        // A part of a stage
+  static constexpr int HALF = BN * BK * 2;          // B part of a stage: 32 KB
+  static constexpr int STAGE = HALF_A + HALF;       // bytes of each of the two LDS stage objects
+  static_assert(BM == 128 || BM == 256, "tile height");
 
   static FC_DEVICE int off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
-  // Wave w fills 1 KB blocks w, w + 8, w + 16, w + 24 (8 rows each) of both operands.
+  // Wave w fills 1 KB blocks (8 rows each) w, w + 8, ... of both operands.
   static FC_DEVICE void dma(char* stage, __amdgpu_buffer_rsrc_t da, int lda, __amdgpu_buffer_rsrc_t db,
                             int ldb, int m0, int n0, int k0, int wave, int lane) {
 #pragma unroll
@@ -180,9 +183,10 @@ struct Gemm8 {
       const int blk = wave + 8 * j;
       const int row = blk * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((row >> 1) & 7);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(da, (lds_void_t*)(stage + blk * 1024), 16,
-                                               ((m0 + row) * lda + k0 + c * 8) * 2, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(db, (lds_void_t*)(stage + HALF + blk * 1024), 16,
+      if (j < BM / 64)  // BM/8 blocks of A: 4 per wave (BM 256) or 2 (BM 128)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(da, (lds_void_t*)(stage + blk * 1024), 16,
+                                                 ((m0 + row) * lda + k0 + c * 8) * 2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(db, (lds_void_t*)(stage + HALF_A + blk * 1024), 16,
                                                ((n0 + row) * ldb + k0 + c * 8) * 2, 0, 0, 0);
     }
   }
@@ -193,10 +197,10 @@ struct Gemm8 {
     const int lr = lane & 31, c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      af[mb] = as_bf16x8(*(const u32x4_t*)(stage + off(wm * 64 + mb * 32 + lr, c)));
+      af[mb] = as_bf16x8(*(const u32x4_t*)(stage + off(wm * WROWS + mb * 32 + lr, c)));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      bfr[nb] = as_bf16x8(*(const u32x4_t*)(stage + HALF + off(wn * 128 + nb * 32 + lr, c)));
+      bfr[nb] = as_bf16x8(*(const u32x4_t*)(stage + HALF_A + off(wn * 128 + nb * 32 + lr, c)));
   }
 
   static FC_DEVICE void mma(const bf16x8_t (&af)[MB], const bf16x8_t (&bfr)[NB], f32x16_t (&acc)[MB][NB]) {
@@ -274,3 +278,25 @@ struct Gemm8 {
     __syncthreads();
   }
 };
+
+// Tile height of Gemm8 for an M-row product with n_tiles_n 256-wide column tiles:
+// the one with fewer rounds of workgroups over the device's CUs, weighting a
+// 128-row tile at 0.72 of a 256-row one (measured: 0.70 at M = 4096).
+#ifndef FC_GEMM8_FORCE_BM
+inline int gemm8_pick_bm(int M, int n_tiles_n) {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n_cu = v;
+    else
+      n_cu = 256;
+  }
+  const long t256 = (long)((M + 255) / 256) * n_tiles_n, t128 = (long)((M + 127) / 128) * n_tiles_n;
+  const long r256 = (t256 + n_cu - 1) / n_cu, r128 = (t128 + n_cu - 1) / n_cu;
+  return r128 * 72 < r256 * 100 ? 128 : 256;
+}
+#else
+inline int gemm8_pick_bm(int, int) { return FC_GEMM8_FORCE_BM; }
+#endif

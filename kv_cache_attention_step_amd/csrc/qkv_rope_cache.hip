@@ -23,7 +23,7 @@
 
 namespace {
 
-constexpr int QKV_BM = 256, QKV_BN = 256;
+constexpr int QKV_BN = 256;
 
 FC_DEVICE int find_seq(const int32_t* __restrict__ cu, int B, int row) {
   int lo = 0, hi = B;  // invariant: cu[lo] <= row < cu[hi]
@@ -51,6 +51,7 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ positions, int T, 
   table[(size_t)t * half + 2 * (e % q) + e / q] = make_float2((float)cs, (float)sn);
 }
 
+template <int BM>
 __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     const uint16_t* __restrict__ hidden, const int32_t* __restrict__ positions,
     const int32_t* __restrict__ cu_q, int B, int M, const uint16_t* __restrict__ w, int d, int H,
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     const int32_t* __restrict__ block_table, int maxp, int log2ps, uint16_t* __restrict__ q_out,
     int32_t* __restrict__ slot_mapping, const float2* __restrict__ rope,
     const float* __restrict__ row_scale, int n_tiles_n) {
-  using G = Gemm8;
+  using G = Gemm8<BM>;
   constexpr int D = 128;
   // two K-slice stages, kept as distinct objects (see Gemm8)
   __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
@@ -68,17 +69,17 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
   // take different weight column blocks, so each XCD streams a disjoint slice of W.
   const int nt = blockIdx.x % n_tiles_n;
   const int mt = blockIdx.x / n_tiles_n;
-  const int m0 = mt * QKV_BM, n0 = nt * QKV_BN;
+  const int m0 = mt * BM, n0 = nt * QKV_BN;
 
   f32x16_t acc[G::MB][G::NB];
   G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, st0, st1, acc);
 
   // token positions and cache slots of this tile's rows
   int* s_pos = (int*)st0;
-  int* s_slot = s_pos + QKV_BM;
+  int* s_slot = s_pos + BM;
   const int t = threadIdx.x;
   const int ps_mask = (1 << log2ps) - 1;
-  if (t < QKV_BM) {
+  if (t < BM) {
     const int row = m0 + t;
     int p = 0, slot = 0;
     if (row < M) {
@@ -107,7 +108,9 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
   // their 64-byte halves, so the two row groups of a write phase fall on
   // different banks), then 16-byte row chunks out, 16 lanes per row: every
   // store writes whole 128-byte lines. Q and K are rotated, V is not.
-  char* tile = st1 + wave * (32 * 256);
+  // (BM 128: the second stage holds waves 0-5, the first one waves 6 and 7
+  // behind the row positions and slots)
+  char* tile = (BM == 256 || wave < 6) ? st1 + wave * (32 * 256) : st0 + (wave - 4) * (32 * 256);
   uint16_t* cache = region == 1 ? kc : vc;
   const bool rot = region < 2;
 #pragma unroll
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = min(m0 + wm * 64 + acc_row(mb, i, lane), M - 1);
+      const int row = min(m0 + wm * G::WROWS + acc_row(mb, i, lane), M - 1);
       const float r = row_scale ? row_scale[row] : 1.f;  // (x r) W^T = r (x W^T)
       // (cos, sin) of pairs lr and lr + 32
       const float4 cs2 = *(const float4*)(rope + (size_t)row * (D / 2) + 2 * lr);
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
       const int q = lane + 64 * j;
       const int rr = q >> 4, c = q & 15;
       const u32x4_t v = *(const u32x4_t*)(tile + rr * 256 + ((c * 16) ^ (((rr >> 2) & 1) << 6)));
-      const int rl = wm * 64 + mb * 32 + rr;
+      const int rl = wm * G::WROWS + mb * 32 + rr;
       const int row = m0 + rl;
       if (row < M) {
         uint16_t* dst;
@@ -313,16 +316,20 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
     FC_REQUIRE((mis & 15) == 0, FC_ERR_INVALID_VALUE,
                "fc_qkv_rope_cache_write: bf16 device pointers must be 16-byte aligned");
     const int n_tiles_n = (write_cache ? 3 * d_model : d_model) / QKV_BN;
-    const int n_tiles_m = (T_q + QKV_BM - 1) / QKV_BM;
+    const int bm = gemm8_pick_bm(T_q, n_tiles_n);
+    const int n_tiles_m = (T_q + bm - 1) / bm;
     const int n_rot = T_q * (head_dim / 2);
     hipLaunchKernelGGL(rope_table_kernel, dim3((n_rot + 255) / 256), dim3(256), 0, st, positions,
                        T_q, head_dim / 2, rope_base, (float2*)workspace);
-    hipLaunchKernelGGL(qkv_rope_cache_bf16_d128, dim3(n_tiles_m * n_tiles_n), dim3(512), 0, st,
-                       (const uint16_t*)hidden, positions, cu_seqlens_q, B, T_q,
-                       (const uint16_t*)w_qkv, d_model, n_heads, rope_base, (uint16_t*)k_cache,
-                       (uint16_t*)v_cache, block_table, max_pages_per_seq, log2ps,
-                       (uint16_t*)q_out, slot_mapping, (const float2*)workspace, row_scale,
-                       n_tiles_n);
+#define FC_QKV_LAUNCH(BMV)                                                                      \
+    hipLaunchKernelGGL(qkv_rope_cache_bf16_d128<BMV>, dim3(n_tiles_m * n_tiles_n), dim3(512), 0, \
+                       st, (const uint16_t*)hidden, positions, cu_seqlens_q, B, T_q,              \
+                       (const uint16_t*)w_qkv, d_model, n_heads, rope_base, (uint16_t*)k_cache,   \
+                       (uint16_t*)v_cache, block_table, max_pages_per_seq, log2ps,                \
+                       (uint16_t*)q_out, slot_mapping, (const float2*)workspace, row_scale,       \
+                       n_tiles_n)
+    if (bm == 128) FC_QKV_LAUNCH(128); else FC_QKV_LAUNCH(256);
+#undef FC_QKV_LAUNCH
     return fc_check_launch("fc_qkv_rope_cache_write");
   }
   FC_REQUIRE(head_dim == 64 || head_dim == 128, FC_ERR_UNSUPPORTED,

@@ -213,13 +213,17 @@ def test_topk_kernel_planted_ties(torch_cuda):
                                                                         nan=-1)), f"k={k} scores"
 
 
-def test_linear_residual_bf16(torch_cuda):
+@pytest.mark.parametrize("M,N,K", [
+    (300, 512, 1024),     # 128-row DMA tiles, ragged last row tile
+    (1100, 12288, 256),   # 256-row DMA tiles (enough column tiles to fill the CUs)
+    (300, 384, 1024),     # width not a multiple of 256: register-staged 128 x 128 tiles
+])
+def test_linear_residual_bf16(torch_cuda, M, N, K):
     torch = torch_cuda
     from kv_cache_attention_step_amd import flashcache as fc
     from kv_cache_attention_step_amd.runner import to_device, to_host
-    _say("case linear residual bf16 300x512x1024")
+    _say(f"case linear residual bf16 {M}x{N}x{K}")
     rng = W.rng_for(9, 1)
-    M, N, K = 300, 512, 1024
     x = W.to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
     w = W.to_bf16_bits((rng.standard_normal((N, K), dtype=np.float32) * 0.02).astype(np.float32))
     h = W.to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
