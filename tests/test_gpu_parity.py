@@ -163,6 +163,36 @@ def test_c2_full_size_sampled(torch_cuda):
                                r["importance"].sum(0), s["cand"], cfg.track, f"topk seq {b}")
 
 
+def test_c2_shaped_ragged_row_tiles(torch_cuda):
+    """C2-shaped layers with 9 sequences (1152 query tokens): the projection runs
+    256-row tiles (fewer rounds of workgroups than 128-row ones) and the last row
+    tile is half empty; sequences at both ends and the one crossing that tile's
+    first row are checked in full against the oracle."""
+    _say("case C2-shaped, 9 sequences (ragged 256-row tiles)")
+    cfg = dataclasses.replace(CF.C2, name="C2-9", seed=57, batch=9)
+    inp = W.make_step_inputs(cfg)
+    assert inp.T_q == 1152
+    got = run_gpu_step(inp, torch_cuda)
+    dt = cfg.dtype
+    H, D = cfg.n_heads, cfg.head_dim
+    for b in (0, 4, 8):   # sequence 8 holds rows 1024..1151: the partial tile
+        s = PU.compact_sequence(inp, b)
+        r = O.flash_cache_step(s["hidden"], s["positions"], s["cu_q"], s["cu_k"], inp.w_qkv, H, D,
+                               cfg.rope_base, s["k_cache"], s["v_cache"], s["block_table"],
+                               cfg.page_size, s["cand"], cfg.track, dt)
+        q0, q1 = s["q0"], s["q1"]
+        slot_real = s["pages"][r["slot_mapping"] // cfg.page_size] * cfg.page_size + \
+            r["slot_mapping"] % cfg.page_size
+        assert np.array_equal(got["slot_mapping"][q0:q1].astype(np.int64), slot_real)
+        PU.assert_close(PU.as_f64(got["q_out"][q0:q1], dt), r["q"], dt, f"q_out seq {b}")
+        pg, off = slot_real // cfg.page_size, slot_real % cfg.page_size
+        PU.assert_close(PU.as_f64(got["k_cache"][pg, :, off, :], dt), r["k"], dt, f"k seq {b}")
+        PU.assert_close(PU.as_f64(got["v_cache"][pg, :, off, :], dt), r["v"], dt, f"v seq {b}")
+        PU.assert_close(PU.as_f64(got["attn_out"][q0:q1], dt), r["out"], dt, f"attn seq {b}")
+        k0, k1 = int(inp.cu_seqlens_k[b]), int(inp.cu_seqlens_k[b + 1])
+        PU.assert_importance_close(got["importance"][:, k0:k1], r["importance"], f"imp seq {b}")
+
+
 def test_c2_deterministic(torch_cuda):
     """Same inputs twice -> bit-identical outputs (no float atomics anywhere)."""
     _say("case C2 determinism")
