@@ -153,6 +153,70 @@ def verify_component(torch, args):
             "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def verify_attention_component(torch, args):
+    """Attention of the verify-shaped step (B=32, 4096-key caches): both views of
+    each sequence (2 x 16..128 query rows, the same draws as the accept test)
+    attend to the sequence's paged cache with a one-pass softmax and no
+    importance. Cache, queries and page table are drawn on the device (values do
+    not change the kernel's work); timed with HIP events like the accept test."""
+    import math
+    import numpy as np
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd import flashcache as fc
+    from kv_cache_attention_step_amd import workload as W
+    cfg = CF.C4
+    rng = W.rng_for(cfg.seed, 0)
+    W.draw_lengths(cfg, rng)
+    L = np.full(cfg.batch, cfg.cache_len_fixed)
+    table, num_pages = W.draw_paging(cfg, L, rng)
+    vlen = rng.integers(cfg.verify_len[0], cfg.verify_len[1] + 1, size=cfg.batch)
+    Qb = 2 * vlen
+    dev = "cuda:0"
+    B, H, D, ps = cfg.batch, cfg.n_heads, cfg.head_dim, cfg.page_size
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(Qb)]), dtype=torch.int32, device=dev)
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum(L)]), dtype=torch.int32, device=dev)
+    T_q, T_k = int(Qb.sum()), int(L.sum())
+    bt = torch.tensor(table, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(cfg.seed + 1)
+    kc = (torch.randn((num_pages, H, ps, D), generator=gen, device=dev) * cfg.kv_std).to(torch.bfloat16)
+    vc = (torch.randn((num_pages, H, ps, D), generator=gen, device=dev) * cfg.kv_std).to(torch.bfloat16)
+    q = torch.randn((T_q, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    wsb = fc.fc_attention_workspace_size(B, T_q, T_k, H, D, 0)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def call():
+        fc.fc_varlen_bidir_attention(q, kc, vc, bt, table.shape[1], ps, cu_q, cu_k, B,
+                                     int(Qb.max()), T_k, H, D, 1.0 / math.sqrt(D), out, None, 0,
+                                     ws, wsb, fc.FC_DTYPE_BF16, stream)
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s / 2:
+        for _ in range(10):
+            with torch.cuda.stream(stream):
+                flush.fill_(3)
+            call()
+        torch.cuda.synchronize()
+    ts = []
+    for i in range(args.warmup + args.steps):
+        with torch.cuda.stream(stream):
+            flush.fill_(3)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        if i >= args.warmup:
+            ts.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e3
+    nbytes = 2.0 * T_k * H * D * 2 + 2.0 * T_q * H * D * 2
+    del kc, vc
+    return {"query_rows": T_q, "cache_tokens": T_k, "avg_us": round(us, 2),
+            "algorithmic_bytes": nbytes, "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def stack_main(args):
     """Layer-stack workload: 32 layers x 32 block-wise denoising steps of one
     512-token generation (B=32). Prints one JSON line with the time per denoising
@@ -294,6 +358,7 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["frac"],
                 "traffic": kd["traffic_bytes"]}
     verify = None if args.no_verify else verify_component(torch, args)
+    verify_attn = None if args.no_verify else verify_attention_component(torch, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seqs)
@@ -320,6 +385,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "verify_accept_c4": verify,
+        "verify_attention_c4": verify_attn,
         "settle": {"seconds": args.settle_s, "steps": settle_steps},
         "step_ms_min": round(float(step_ms.min()), 4),
         "wall_s_timed_loop": round(wall, 4),

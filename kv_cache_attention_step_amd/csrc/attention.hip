@@ -302,9 +302,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
     rt_begin = 0;
     rt_end = a.n_rt;
   } else {
-    rt_begin = item % a.n_rt;
+    // the row tiles of one (sequence, head) are 8 block indices apart: the same
+    // XCD (workgroups go to the XCDs round-robin), dispatched together, so the
+    // K/V stream of one is served from that XCD's L2 for the others
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    rt_begin = slot % a.n_rt;
     rt_end = rt_begin + 1;
-    item /= a.n_rt;
+    item = (slot / a.n_rt) * 8 + xcd;
+    if (item >= a.B * a.H) return;
   }
   const int sr = item / a.H;
   const int h = item % a.H;
@@ -716,7 +721,9 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
     a.scale_log2 = softmax_scale * LOG2E;
     hipLaunchKernelGGL(lpt_order, dim3(1), dim3(256), 0, st, cu_seqlens_k, B, (int32_t*)workspace);
     const bool ps16 = page_size >= 16;
-    const dim3 grid(importance ? B * n_heads : B * n_heads * a.n_rt);
+    // one-pass: (sequence, head) items in groups of 8, one per XCD, each group's
+    // row tiles consecutive per XCD (see the kernel's block mapping)
+    const dim3 grid(importance ? B * n_heads : ((B * n_heads + 7) / 8) * 8 * a.n_rt);
 #define FC_ATTN_LAUNCH(IMP, PS, KSP) \
     hipLaunchKernelGGL((attn_bf16_d128<IMP, PS, KSP>), grid, dim3(256), 0, st, a)
     if (importance) {
