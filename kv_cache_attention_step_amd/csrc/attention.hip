@@ -66,10 +66,29 @@ struct AttnArgs {
   uint16_t* out;
   float* imp;
   int maxp, log2ps, B, H, T_k, n_rt, accumulate;
+  int lpt_inline;         // order == NULL and B <= 64: each workgroup ranks the sequences
   float scale_log2;  // softmax_scale * log2(e)
 };
 
 FC_DEVICE float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The sequence at position sr of the longest-first order (by cache length;
+// equal lengths keep their index order), for B <= 64: lane b ranks sequence b
+// and the wave picks the lane whose rank is sr. Every wave computes it, so no
+// ordering kernel has to run first.
+FC_DEVICE int lpt_sequence(const int32_t* __restrict__ cu_k, int B, int sr) {
+  const int lane = threadIdx.x & 63;
+  int rank = -1;
+  if (lane < B) {
+    const int Lb = cu_k[lane + 1] - cu_k[lane];
+    rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const int Lj = cu_k[j + 1] - cu_k[j];
+      rank += (Lj > Lb) || (Lj == Lb && j < lane);
+    }
+  }
+  return (int)__builtin_ctzll(__ballot(rank == sr));
+}
 
 
 // ---- tile loads ----------------------------------------------------------
@@ -313,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
   }
   const int sr = item / a.H;
   const int h = item % a.H;
-  const int b = a.order ? a.order[sr] : sr;
+  const int b = a.order ? a.order[sr] : (a.lpt_inline ? lpt_sequence(a.cu_k, a.B, sr) : sr);
   const int q0 = a.cu_q[b], Q = a.cu_q[b + 1] - q0;
   const int k0 = a.cu_k[b], L = a.cu_k[b + 1] - k0;
   const int t = threadIdx.x, lane = t & 63;
@@ -719,7 +738,11 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
     a.n_rt = ks ? 1 : (max_seqlen_q + AROWS - 1) / AROWS;
     a.accumulate = accumulate ? 1 : 0;
     a.scale_log2 = softmax_scale * LOG2E;
-    hipLaunchKernelGGL(lpt_order, dim3(1), dim3(256), 0, st, cu_seqlens_k, B, (int32_t*)workspace);
+    a.lpt_inline = B <= 64;
+    if (a.lpt_inline)
+      a.order = nullptr;
+    else
+      hipLaunchKernelGGL(lpt_order, dim3(1), dim3(256), 0, st, cu_seqlens_k, B, (int32_t*)workspace);
     const bool ps16 = page_size >= 16;
     // one-pass: (sequence, head) items in groups of 8, one per XCD, each group's
     // row tiles consecutive per XCD (see the kernel's block mapping)
