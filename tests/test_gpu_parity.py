@@ -106,6 +106,16 @@ def test_small_page_size_path(torch_cuda):
     full_parity(inp, got)
 
 
+def test_large_page_size_path(torch_cuda):
+    """page_size 64: four 16-key load groups share a page; the last page of a
+    sequence is partly past its end (NaN tails there must never be read)."""
+    cfg = dataclasses.replace(SMALL_BF16, name="C2-ps64", seed=26, page_size=64)
+    _say("case C2-small bf16, page size 64, NaN tails")
+    inp = W.make_step_inputs(cfg, tail_nan=True)
+    got = run_gpu_step(inp, torch_cuda)
+    full_parity(inp, got)
+
+
 def test_bf16_query_longer_than_one_row_tile(torch_cuda):
     """Q_b > 128 rows: the importance path loops over row tiles in one workgroup."""
     cfg = dataclasses.replace(SMALL_BF16, name="C2-rows", seed=22, batch=2, prompt=(100, 180),
