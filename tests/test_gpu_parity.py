@@ -116,6 +116,18 @@ def test_large_page_size_path(torch_cuda):
     full_parity(inp, got)
 
 
+def test_many_sequences(torch_cuda):
+    """70 sequences: more than one wave can rank, so the longest-first order comes
+    from the ordering kernel instead of each attention workgroup."""
+    cfg = dataclasses.replace(SMALL_BF16, name="C2-many", seed=27, batch=70, prompt=(20, 90),
+                              gen_len=48, window=16, track=12)
+    _say("case 70 sequences")
+    inp = W.make_step_inputs(cfg)
+    assert inp.B > 64
+    got = run_gpu_step(inp, torch_cuda)
+    full_parity(inp, got)
+
+
 def test_bf16_query_longer_than_one_row_tile(torch_cuda):
     """Q_b > 128 rows: the importance path loops over row tiles in one workgroup."""
     cfg = dataclasses.replace(SMALL_BF16, name="C2-rows", seed=22, batch=2, prompt=(100, 180),
