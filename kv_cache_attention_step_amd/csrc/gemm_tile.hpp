@@ -145,7 +145,8 @@ FC_DEVICE int acc_col(int nb, int lane) { return nb * 32 + (lane & 31); }
 //
 // Operands travel global -> LDS by the buffer unit's direct-to-LDS loads (no
 // staging registers) in K-slices of 64: a stage is A (BM rows x 128 bytes) then
-// B (256 rows x 128 bytes), 64 or 48 KB, and two stages alternate. A load instruction
+// B (256 rows x 128 bytes), 64 or 48 KB; two (BM 256) or three (BM 128) stages
+// rotate, so a slice is requested one or two slices before it is consumed. A load instruction
 // moves 8 rows x 128 bytes, so every group of 8 lanes fetches one whole
 // 128-byte line: L2 serves such a stream at close to twice the rate of 64-byte
 // row pieces. Within a row, 16-byte chunk c sits at position c ^ ((row >> 1) & 7)
@@ -156,7 +157,7 @@ FC_DEVICE int acc_col(int nb, int lane) { return nb * 32 + (lane & 31); }
 // 4-7 (the second half) put one wave of each group on every SIMD and run half a period apart,
 // separated by s_barrier. In its memory phase a wave reads the fragments of one
 // 32-wide half-slice (both k16 steps) and, on the first half of a slice, issues
-// the next slice into the other stage; in its compute phase it issues the 16
+// the slice NST - 1 ahead into the stage just freed; in its compute phase it issues the 16
 // MFMAs of that half-slice. So one wave of each SIMD feeds the matrix unit while
 // the other one waits on LDS and memory. A stage is refilled only after both
 // groups have read it (the memory phase ends with lgkmcnt(0) before its barrier)
@@ -170,7 +171,10 @@ struct Gemm8 {
   static constexpr int WROWS = BM / 4;              // tile rows of one wave
   static constexpr int HALF_A = BM * BK * 2;        // A part of a stage
   static constexpr int HALF = BN * BK * 2;          // B part of a stage: 32 KB
-  static constexpr int STAGE = HALF_A + HALF;       // bytes of each of the two LDS stage objects
+  static constexpr int STAGE = HALF_A + HALF;       // bytes of each LDS stage object
+  // stages: two of 64 KB (BM 256), three of 48 KB (BM 128): 128 or 144 KB of LDS
+  static constexpr int NST = BM == 128 ? 3 : 2;
+  static constexpr int DMA_N = BM / 64 + 4;         // direct-to-LDS loads per wave per slice
   static_assert(BM == 128 || BM == 256, "tile height");
 
   static FC_DEVICE int off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
@@ -225,16 +229,18 @@ struct Gemm8 {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // K must be a multiple of 128. st0, st1: two distinct __shared__ arrays of
+  // K must be a multiple of 64. st[0 .. NST-1]: distinct __shared__ arrays of
   // STAGE bytes (distinct objects, so the compiler sees that fragment reads of
-  // one stage do not depend on loads landing in the other and adds no wait of
-  // its own). Past the last slice the refill goes through a zero-range buffer
-  // descriptor (no memory access), so every slice issues the same loads and the
-  // wait counts are constants. Ends with every load landed and a barrier, so
-  // the caller may reuse the stages.
+  // one stage do not depend on loads landing in another and adds no wait of its
+  // own); slice s lives in stage s mod NST and is requested NST - 1 slices ahead.
+  // The slice count is padded to a multiple of NST: past the last slice the
+  // loads go through a zero-range buffer descriptor (no memory access) and the
+  // MFMAs are skipped, so every slice issues the same loads and the wait counts
+  // are constants. Ends with every load landed and a barrier, so the caller may
+  // reuse the stages.
   static FC_DEVICE void run(const uint16_t* __restrict__ A, int lda, int M,
                             const uint16_t* __restrict__ Bm, int ldb, int N, int K, int m0, int n0,
-                            char* st0, char* st1, f32x16_t (&acc)[MB][NB]) {
+                            char* const (&st)[3], f32x16_t (&acc)[MB][NB]) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -248,29 +254,37 @@ struct Gemm8 {
     const __amdgpu_buffer_rsrc_t db = make_rsrc(Bm, (uint32_t)N * ldb * 2);
     const __amdgpu_buffer_rsrc_t dz = make_rsrc(A, 0);
     const int KS = K / BK;
-    dma(st0, da, lda, db, ldb, m0, n0, 0, wave, lane);
-    FC_WAIT_VMCNT(0);
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j) {
+      const bool more = j < KS;
+      dma(st[j], more ? da : dz, lda, more ? db : dz, ldb, m0, n0, j * BK, wave, lane);
+    }
+    FC_WAIT_VMCNT((NST - 2) * DMA_N);  // slice 0 landed (for this wave)
     lds_bar();
     bf16x8_t a0[MB], b0[NB], a1[MB], b1[NB];
-    if (wm >= 2) bar();  // rows 128-255 start half a period later
-    for (int w = 0; w < KS; w += 2) {
+    if (wm >= 2) bar();  // the second half of the tile rows starts half a period later
+    for (int w = 0; w < KS; w += NST) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {  // half-slices of slices w (stage 0) and w + 1 (stage 1)
-        char* cur = q < 2 ? st0 : st1;
-        char* oth = q < 2 ? st1 : st0;
-        const int ws = w + (q >> 1);
+      for (int q = 0; q < 2 * NST; ++q) {  // half-slices of slices w .. w + NST - 1
+        const int j = q >> 1;
+        const int ws = w + j;
+        char* cur = st[j];
         // memory phase
         if ((q & 1) == 0) {
-          const bool more = ws + 1 < KS;
-          dma(oth, more ? da : dz, lda, more ? db : dz, ldb, m0, n0, (ws + 1) * BK, wave, lane);
+          const int nxt = ws + NST - 1;
+          const bool more = nxt < KS;
+          dma(st[(j + NST - 1) % NST], more ? da : dz, lda, more ? db : dz, ldb, m0, n0, nxt * BK,
+              wave, lane);
         }
         frags(cur, 2 * (q & 1), wm, wn, lane, a0, b0);
         frags(cur, 2 * (q & 1) + 1, wm, wn, lane, a1, b1);
-        if (q & 1) FC_WAIT_VMCNT(0);  // slice ws + 1 landed (for this wave)
+        if (q & 1) FC_WAIT_VMCNT((NST - 2) * DMA_N);  // slice ws + 1 landed (for this wave)
         lds_bar();
         // compute phase
-        mma(a0, b0, acc);
-        mma(a1, b1, acc);
+        if (ws < KS) {
+          mma(a0, b0, acc);
+          mma(a1, b1, acc);
+        }
         bar();
       }
     }
@@ -281,7 +295,8 @@ struct Gemm8 {
 
 // Tile height of Gemm8 for an M-row product with n_tiles_n 256-wide column tiles:
 // the one with fewer rounds of workgroups over the device's CUs, weighting a
-// 128-row tile at 0.72 of a 256-row one (measured: 0.70 at M = 4096).
+// 128-row tile (three stages) at 0.62 of a 256-row one (two stages): measured
+// 0.58 to 0.63 for M from 1024 to 8192 with 16 or 48 column tiles.
 #ifndef FC_GEMM8_FORCE_BM
 inline int gemm8_pick_bm(int M, int n_tiles_n) {
   static int n_cu = 0;
@@ -295,7 +310,7 @@ inline int gemm8_pick_bm(int M, int n_tiles_n) {
   }
   const long t256 = (long)((M + 255) / 256) * n_tiles_n, t128 = (long)((M + 127) / 128) * n_tiles_n;
   const long r256 = (t256 + n_cu - 1) / n_cu, r128 = (t128 + n_cu - 1) / n_cu;
-  return r128 * 72 < r256 * 100 ? 128 : 256;
+  return r128 * 62 < r256 * 100 ? 128 : 256;
 }
 #else
 inline int gemm8_pick_bm(int, int) { return FC_GEMM8_FORCE_BM; }

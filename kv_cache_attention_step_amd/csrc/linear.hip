@@ -49,11 +49,13 @@ __global__ __launch_bounds__(512, 1) void linear_residual_dma(const uint16_t* __
   using G = Gemm8<BM>;
   __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[G::NST > 2 ? G::STAGE : 1024];
+  char* const sts[3] = {st0, st1, st2};
   const int nt = blockIdx.x % n_tiles_n;
   const int mt = blockIdx.x / n_tiles_n;
   const int m0 = mt * BM, n0 = nt * G::BN;
   f32x16_t acc[G::MB][G::NB];
-  G::run(x, K, M, w, K, N, K, m0, n0, st0, st1, acc);
+  G::run(x, K, M, w, K, N, K, m0, n0, sts, acc);
 
   const int lane = threadIdx.x & 63, lr = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -61,9 +61,11 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
     const float* __restrict__ row_scale, int n_tiles_n) {
   using G = Gemm8<BM>;
   constexpr int D = 128;
-  // two K-slice stages, kept as distinct objects (see Gemm8)
+  // K-slice stages, kept as distinct objects (see Gemm8); the third is used by 128-row tiles only
   __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[G::NST > 2 ? G::STAGE : 1024];
+  char* const sts[3] = {st0, st1, st2};
 
   // N-tile fastest: consecutive workgroups (spread over the XCDs round-robin)
   // take different weight column blocks, so each XCD streams a disjoint slice of W.
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
   const int m0 = mt * BM, n0 = nt * QKV_BN;
 
   f32x16_t acc[G::MB][G::NB];
-  G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, st0, st1, acc);
+  G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, sts, acc);
 
   // token positions and cache slots of this tile's rows
   int* s_pos = (int*)st0;
@@ -108,9 +110,8 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
   // their 64-byte halves, so the two row groups of a write phase fall on
   // different banks), then 16-byte row chunks out, 16 lanes per row: every
   // store writes whole 128-byte lines. Q and K are rotated, V is not.
-  // (BM 128: the second stage holds waves 0-5, the first one waves 6 and 7
-  // behind the row positions and slots)
-  char* tile = (BM == 256 || wave < 6) ? st1 + wave * (32 * 256) : st0 + (wave - 4) * (32 * 256);
+  // (BM 128: the second stage holds waves 0-5, the third one waves 6 and 7)
+  char* tile = (BM == 256 || wave < 6) ? st1 + wave * (32 * 256) : st2 + (wave - 6) * (32 * 256);
   uint16_t* cache = region == 1 ? kc : vc;
   const bool rot = region < 2;
 #pragma unroll
