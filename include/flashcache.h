@@ -110,8 +110,9 @@ const char* fc_version(void);
  *               hidden[t] * row_scale[t] (an input normalisation computed by
  *               fc_rms_row_scale)
  * workspace     device memory of at least fc_qkv_workspace_size() bytes (the
- *               per-token rotation table; overwritten; NULL allowed when that
- *               size is 0; calls that overlap on one workspace race)
+ *               per-token rotation table and cache slots; overwritten; NULL
+ *               allowed when that size is 0; calls that overlap on one
+ *               workspace race)
  * Supported: bf16 with D = 128 and d a multiple of 256; f32 with D in {64,128}.
  * page_size must be a power of two in [1, 256]. bf16: hidden, w_qkv, q_out,
  * k_cache, v_cache and workspace must be 16-byte aligned (FC_ERR_INVALID_VALUE

@@ -238,9 +238,38 @@ struct Gemm8 {
   // MFMAs are skipped, so every slice issues the same loads and the wait counts
   // are constants. Ends with every load landed and a barrier, so the caller may
   // reuse the stages.
+  // Requests the first NST - 1 slices (the part of run() that may be issued
+  // early, e.g. before the previous tile's epilogue).
+  static FC_DEVICE void prologue(const uint16_t* __restrict__ A, int lda, int M,
+                                 const uint16_t* __restrict__ Bm, int ldb, int N, int K, int m0,
+                                 int n0, char* const (&st)[3]) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const __amdgpu_buffer_rsrc_t da = make_rsrc(A, (uint32_t)M * lda * 2);
+    const __amdgpu_buffer_rsrc_t db = make_rsrc(Bm, (uint32_t)N * ldb * 2);
+    const __amdgpu_buffer_rsrc_t dz = make_rsrc(A, 0);
+    const int KS = K / BK;
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j) {
+      const bool more = j < KS;
+      dma(st[j], more ? da : dz, lda, more ? db : dz, ldb, m0, n0, j * BK, wave, lane);
+    }
+  }
+
   static FC_DEVICE void run(const uint16_t* __restrict__ A, int lda, int M,
                             const uint16_t* __restrict__ Bm, int ldb, int N, int K, int m0, int n0,
                             char* const (&st)[3], f32x16_t (&acc)[MB][NB]) {
+    prologue(A, lda, M, Bm, ldb, N, K, m0, n0, st);
+    main_loop<false>(A, lda, M, Bm, ldb, N, K, m0, n0, st, acc);
+  }
+
+  // The rest of run() after prologue(). AFTER_OTHER: other vector memory
+  // operations were issued after the prologue (a previous tile's epilogue), so
+  // the first wait is for everything outstanding.
+  template <bool AFTER_OTHER>
+  static FC_DEVICE void main_loop(const uint16_t* __restrict__ A, int lda, int M,
+                                  const uint16_t* __restrict__ Bm, int ldb, int N, int K, int m0,
+                                  int n0, char* const (&st)[3], f32x16_t (&acc)[MB][NB]) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -254,12 +283,10 @@ struct Gemm8 {
     const __amdgpu_buffer_rsrc_t db = make_rsrc(Bm, (uint32_t)N * ldb * 2);
     const __amdgpu_buffer_rsrc_t dz = make_rsrc(A, 0);
     const int KS = K / BK;
-#pragma unroll
-    for (int j = 0; j < NST - 1; ++j) {
-      const bool more = j < KS;
-      dma(st[j], more ? da : dz, lda, more ? db : dz, ldb, m0, n0, j * BK, wave, lane);
-    }
-    FC_WAIT_VMCNT((NST - 2) * DMA_N);  // slice 0 landed (for this wave)
+    if (AFTER_OTHER)
+      FC_WAIT_VMCNT(0);
+    else
+      FC_WAIT_VMCNT((NST - 2) * DMA_N);  // slice 0 landed (for this wave)
     lds_bar();
     bf16x8_t a0[MB], b0[NB], a1[MB], b1[NB];
     if (wm >= 2) bar();  // the second half of the tile rows starts half a period later
@@ -293,12 +320,8 @@ struct Gemm8 {
   }
 };
 
-// Tile height of Gemm8 for an M-row product with n_tiles_n 256-wide column tiles:
-// the one with fewer rounds of workgroups over the device's CUs, weighting a
-// 128-row tile (three stages) at 0.62 of a 256-row one (two stages): measured
-// 0.58 to 0.63 for M from 1024 to 8192 with 16 or 48 column tiles.
-#ifndef FC_GEMM8_FORCE_BM
-inline int gemm8_pick_bm(int M, int n_tiles_n) {
+// Compute units of the current device (cached; 256 if the query fails).
+inline int fc_num_cus() {
   static int n_cu = 0;
   if (n_cu == 0) {
     int dev = 0, v = 0;
@@ -308,6 +331,16 @@ inline int gemm8_pick_bm(int M, int n_tiles_n) {
     else
       n_cu = 256;
   }
+  return n_cu;
+}
+
+// Tile height of Gemm8 for an M-row product with n_tiles_n 256-wide column tiles:
+// the one with fewer rounds of workgroups over the device's CUs, weighting a
+// 128-row tile (three stages) at 0.62 of a 256-row one (two stages): measured
+// 0.58 to 0.63 for M from 1024 to 8192 with 16 or 48 column tiles.
+#ifndef FC_GEMM8_FORCE_BM
+inline int gemm8_pick_bm(int M, int n_tiles_n) {
+  const int n_cu = fc_num_cus();
   const long t256 = (long)((M + 255) / 256) * n_tiles_n, t128 = (long)((M + 127) / 128) * n_tiles_n;
   const long r256 = (t256 + n_cu - 1) / n_cu, r128 = (t128 + n_cu - 1) / n_cu;
   return r128 * 62 < r256 * 100 ? 128 : 256;

@@ -17,6 +17,8 @@
 // 128-byte lines, to q_out or to the token's cache slot.
 //
 // f32 path (small models): one work-item per (token, head, rotation pair).
+#include <type_traits>
+
 #include "gemm_tile.hpp"
 
 #include <math.h>
@@ -34,32 +36,56 @@ FC_DEVICE int find_seq(const int32_t* __restrict__ cu, int B, int row) {
   return lo;
 }
 
+// Pre-pass of the bf16 path, one thread per (token, rotation pair).
 // Rotation table: (cos, sin) of positions[t] * base^(-2e/D) for pair e of
 // token t, in fp64 then rounded to fp32. One entry per (token, pair); every Q
 // and K head of the token reuses it. Within a token, pairs e and e + half/2
 // are adjacent (entry 2 (e mod half/2) + e div half/2), so the lane that
 // rotates both loads them with one 16-byte load.
-__global__ void rope_table_kernel(const int32_t* __restrict__ positions, int T, int half,
-                                  float rope_base, float2* __restrict__ table) {
+// When a row scale is given, the table holds it folded in (r cos, r sin), so
+// rotated rows need no separate scaling.
+// Cache slots: the thread of pair 0 also resolves token t's page-table entry
+// (its sequence by binary search over cu_q, then the page of its position)
+// once, so the projection's epilogue reads one slot per row instead of running
+// this chain of dependent loads in every column tile.
+__global__ void qkv_prepass_kernel(const int32_t* __restrict__ positions, int T, int half,
+                                   float rope_base, float2* __restrict__ table,
+                                   const int32_t* __restrict__ cu_q, int B,
+                                   const int32_t* __restrict__ block_table, int maxp, int log2ps,
+                                   int32_t* __restrict__ slots, int32_t* __restrict__ slot_mapping,
+                                   const float* __restrict__ row_scale) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * half) return;
   const int t = idx / half, e = idx - t * half;
   const int q = half / 2;
+  const int p = positions[t];
   const double inv_freq = exp2(-(double)e / (double)half * log2((double)rope_base));
   double sn, cs;
-  sincos((double)positions[t] * inv_freq, &sn, &cs);
-  table[(size_t)t * half + 2 * (e % q) + e / q] = make_float2((float)cs, (float)sn);
+  sincos((double)p * inv_freq, &sn, &cs);
+  // with a row scale r (q, k, v of hidden[t] * r) the table holds (r cos, r sin)
+  const double r = row_scale ? (double)row_scale[t] : 1.0;
+  table[(size_t)t * half + 2 * (e % q) + e / q] = make_float2((float)(cs * r), (float)(sn * r));
+  if (e == 0 && block_table) {
+    const int b = find_seq(cu_q, B, t);
+    const int page = block_table[(size_t)b * maxp + (p >> log2ps)];
+    const int slot = (page << log2ps) + (p & ((1 << log2ps) - 1));
+    slots[t] = slot;
+    if (slot_mapping) slot_mapping[t] = slot;
+  }
 }
 
-template <int BM>
-__global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
-    const uint16_t* __restrict__ hidden, const int32_t* __restrict__ positions,
-    const int32_t* __restrict__ cu_q, int B, int M, const uint16_t* __restrict__ w, int d, int H,
-    float rope_base, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ block_table, int maxp, int log2ps, uint16_t* __restrict__ q_out,
-    int32_t* __restrict__ slot_mapping, const float2* __restrict__ rope,
+// bf16, D = 128: one workgroup per 256-wide column tile (two heads of one of
+// Q, K, V) of BM token rows, column tile fastest (consecutive workgroups, spread
+// over the XCDs round-robin, take different weight column blocks, so each XCD
+// streams a disjoint slice of W). The GEMM is one of the tile pipelines of
+// gemm_tile.hpp; a wave owns whole heads, so RoPE needs no exchange between lanes.
+template <class G>
+__global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
+    const uint16_t* __restrict__ hidden, int M, const uint16_t* __restrict__ w, int d, int H,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ slots,
+    int log2ps, uint16_t* __restrict__ q_out, const float2* __restrict__ rope,
     const float* __restrict__ row_scale, int n_tiles_n) {
-  using G = Gemm8<BM>;
+  constexpr int BM = G::BM;
   constexpr int D = 128;
   // K-slice stages, kept as distinct objects (see Gemm8); the third is used by 128-row tiles only
   __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
@@ -67,103 +93,149 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_cache_bf16_d128(
   __shared__ __attribute__((aligned(1024))) char st2[G::NST > 2 ? G::STAGE : 1024];
   char* const sts[3] = {st0, st1, st2};
 
-  // N-tile fastest: consecutive workgroups (spread over the XCDs round-robin)
-  // take different weight column blocks, so each XCD streams a disjoint slice of W.
   const int nt = blockIdx.x % n_tiles_n;
   const int mt = blockIdx.x / n_tiles_n;
   const int m0 = mt * BM, n0 = nt * QKV_BN;
+  const int t = threadIdx.x;
+  // cache slot of tile row t (resolved by the pre-pass), requested before the
+  // main loop so its latency is hidden there
+  int slot_t = 0;
+  if (slots && t < BM && m0 + t < M) slot_t = slots[m0 + t];
 
   f32x16_t acc[G::MB][G::NB];
   G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, sts, acc);
 
-  // token positions and cache slots of this tile's rows
-  int* s_pos = (int*)st0;
-  int* s_slot = s_pos + BM;
-  const int t = threadIdx.x;
-  const int ps_mask = (1 << log2ps) - 1;
-  if (t < BM) {
-    const int row = m0 + t;
-    int p = 0, slot = 0;
-    if (row < M) {
-      p = positions[row];
-      if (block_table) {
-        const int b = find_seq(cu_q, B, row);
-        const int page = block_table[(size_t)b * maxp + (p >> log2ps)];
-        slot = (page << log2ps) + (p & ps_mask);
-        if (nt == 0 && slot_mapping) slot_mapping[row] = slot;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63, lr = lane & 31, h5 = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int col0 = n0 + wn * D;  // first column of this wave's head
+  const int region = col0 / d;   // 0 = Q, 1 = K, 2 = V
+  const int h = (col0 - region * d) / D;
+  const bool rot = region < 2;             // Q and K are rotated, V is not
+  const bool scaled = row_scale != nullptr;
+  const int row0 = m0 + wm * G::WROWS;     // first row of this wave
+  // The matrix unit idles during the epilogue, so it is kept short: addresses
+  // are a per-lane offset plus constants (buffer loads whose range ends at row
+  // M, so rows past it read 0; LDS offsets folded into immediates).
+  const __amdgpu_buffer_rsrc_t rope_r = make_rsrc(rope, (uint32_t)M * (D / 2) * 8);
+  const __amdgpu_buffer_rsrc_t rs_r = make_rsrc(row_scale, (uint32_t)M * 4);
+  // lane rows of an accumulator block: 8 (i / 4) + 4 h5 + i % 4
+  const uint32_t rope_vo = (row0 + 4 * h5) * (D / 2 * 8) + lr * 16;  // (cos, sin) of pairs lr, lr + 32
+  const uint32_t rs_vo = (row0 + 4 * h5) * 4;
+
+  // rotation (Q, K) or row scale (V) of the 16 rows a lane holds in 32-row block mb
+  float4 cs2[16];
+  float rsc[16];
+  auto load_block = [&](int mb, auto rot_c, auto scaled_c) {
+    if (decltype(rot_c)::value) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = mb * 32 + (i >> 2) * 8 + (i & 3);
+        cs2[i] = __builtin_bit_cast(
+            float4, __builtin_amdgcn_raw_buffer_load_b128(rope_r, rope_vo + c * (D / 2 * 8), 0, 0));
       }
     }
-    s_pos[t] = p;
-    s_slot[t] = slot;
-  }
-  __syncthreads();
+    if (decltype(scaled_c)::value) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = mb * 32 + (i >> 2) * 8 + (i & 3);
+        rsc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_r, rs_vo + c * 4, 0, 0));
+      }
+    }
+  };
+  int* s_slot = (int*)st0;
 
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int lane = t & 63, lr = lane & 31;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int col0 = n0 + wn * D;             // first column of this wave's head
-  const int region = col0 / d;              // 0 = Q, 1 = K, 2 = V
-  const int h = (col0 - region * d) / D;
-
-  // Per 32-row block: row scale and RoPE in registers, bf16 values into a
+  // Per 32-row block: RoPE or row scale in registers, bf16 values into a
   // wave-private 8 KB LDS tile (32 rows of 256 bytes; rows with bit 2 set swap
   // their 64-byte halves, so the two row groups of a write phase fall on
   // different banks), then 16-byte row chunks out, 16 lanes per row: every
-  // store writes whole 128-byte lines. Q and K are rotated, V is not.
-  // (BM 128: the second stage holds waves 0-5, the third one waves 6 and 7)
-  char* tile = (BM == 256 || wave < 6) ? st1 + wave * (32 * 256) : st2 + (wave - 6) * (32 * 256);
+  // store writes whole 128-byte lines.
+  // (8 waves of a 128-row tile: the second stage holds waves 0-5, the third one waves 6 and 7)
+  constexpr bool one_stage = G::STAGE >= (G::THREADS / 64) * 32 * 256;
+  char* tile = (one_stage || wave < 6) ? st1 + wave * (32 * 256) : st2 + (wave - 6) * (32 * 256);
+  // write side: row 8 (i / 4) + 4 h5 + i % 4, column nb * 32 + lr; the half
+  // swap (bit 6 of the byte offset, set by h5) permutes the column blocks
+  char* const wb0 = tile + h5 * 1024 + lr * 2 + h5 * 64;         // blocks 0, 2
+  char* const wb1 = tile + h5 * 1024 + lr * 2 + 64 - h5 * 64;    // blocks 1, 3
+  // read side: round j covers rows 4 j + lane / 16, chunk lane % 16 (swap on odd rounds)
+  const int c16 = (lane & 15) * 16, r4 = lane >> 4;
+  const char* const rb0 = tile + r4 * 256 + c16;
+  const char* const rb1 = tile + r4 * 256 + (c16 ^ 64);
   uint16_t* cache = region == 1 ? kc : vc;
-  const bool rot = region < 2;
+  const int ps_mask = (1 << log2ps) - 1;
+  const __amdgpu_buffer_rsrc_t q_r = make_rsrc(q_out, (uint32_t)M * H * D * 2);
+  const uint32_t q_vo = (uint32_t)(row0 + r4) * (H * D * 2) + h * (D * 2) + c16;
+  // K/V rows: byte offset in the cache of (slot, head h, chunk) =
+  // page * (H ps 256) + h (ps 256) + (slot mod ps) 256 + chunk
+  const uint32_t page_bytes = (uint32_t)H << (log2ps + 8);
+  const uint32_t kv_lane = ((uint32_t)h << (log2ps + 8)) + c16;
+  // The rest is instantiated for rotated (Q, K: the row scale is folded into
+  // the rotation table) and plain (V: scaled or not) tiles; the choice is
+  // uniform over the workgroup (a tile lies in one of Q, K, V), and no path
+  // carries another's work or register copies.
+  auto blocks = [&](auto rot_c, auto scaled_c) {
+    constexpr bool ROT = decltype(rot_c)::value, SCALED = decltype(scaled_c)::value;
+    load_block(0, rot_c, scaled_c);
+    if (t < BM) s_slot[t] = slot_t;
+    __syncthreads();
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb) {
-    __builtin_amdgcn_sched_barrier(0);
+    for (int mb = 0; mb < G::MB; ++mb) {
+      __builtin_amdgcn_sched_barrier(0);
+      // rows i and i + 1 at a time: scale, rotate, pack, into the tile (their
+      // accumulators and rotation values die as soon as they are written)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = min(m0 + wm * G::WROWS + acc_row(mb, i, lane), M - 1);
-      const float r = row_scale ? row_scale[row] : 1.f;  // (x r) W^T = r (x W^T)
-      // (cos, sin) of pairs lr and lr + 32
-      const float4 cs2 = *(const float4*)(rope + (size_t)row * (D / 2) + 2 * lr);
+      for (int i = 0; i < 16; i += 2) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        // rotate-half partners e and e + 64 are blocks nb and nb + 2 of the same lane
-        const float2 cs = nb == 0 ? make_float2(cs2.x, cs2.y) : make_float2(cs2.z, cs2.w);
-        const float x = acc[mb][nb][i] * r, y = acc[mb][nb + 2][i] * r;
-        acc[mb][nb][i] = rot ? x * cs.x - y * cs.y : x;
-        acc[mb][nb + 2][i] = rot ? y * cs.x + x * cs.y : y;
-      }
-    }
+        for (int k = i; k < i + 2; ++k) {
+          if (SCALED) {  // (x r) W^T = r (x W^T)
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const int rr = acc_row(0, i, lane);  // rows rr and rr + 1 of the block (same bit 2)
+            for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb][k] *= rsc[k];
+          }
+          if (ROT) {
 #pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb) {
-        const uint32_t p = pack2(acc[mb][nb][i], acc[mb][nb][i + 1]);
-        const int b = ((nb * 32 + lr) * 2) ^ (((rr >> 2) & 1) << 6);
-        *(uint16_t*)(tile + rr * 256 + b) = (uint16_t)p;
-        *(uint16_t*)(tile + (rr + 1) * 256 + b) = (uint16_t)(p >> 16);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's tile writes are done
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = lane + 64 * j;
-      const int rr = q >> 4, c = q & 15;
-      const u32x4_t v = *(const u32x4_t*)(tile + rr * 256 + ((c * 16) ^ (((rr >> 2) & 1) << 6)));
-      const int rl = wm * G::WROWS + mb * 32 + rr;
-      const int row = m0 + rl;
-      if (row < M) {
-        uint16_t* dst;
-        if (region == 0) {
-          dst = q_out + ((size_t)row * H + h) * D;
-        } else {
-          const int slot = s_slot[rl];
-          dst = cache + (((size_t)(slot >> log2ps) * H + h) * (ps_mask + 1) + (slot & ps_mask)) * D;
+            for (int nb = 0; nb < 2; ++nb) {
+              // rotate-half partners e and e + 64 are blocks nb and nb + 2 of the same lane
+              const float x = acc[mb][nb][k], y = acc[mb][nb + 2][k];
+              const float c = nb == 0 ? cs2[k].x : cs2[k].z, sn = nb == 0 ? cs2[k].y : cs2[k].w;
+              acc[mb][nb][k] = x * c - y * sn;
+              acc[mb][nb + 2][k] = y * c + x * sn;
+            }
+          }
         }
-        *(u32x4_t*)(dst + c * 8) = v;
+        const int rc = (i >> 2) * 8 + (i & 3);  // rows rc and rc + 1 (+ 4 h5) of the block
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb) {
+          const uint32_t p = pack2(acc[mb][nb][i], acc[mb][nb][i + 1]);
+          char* const wp = ((nb & 1) ? wb1 : wb0) + rc * 256 + (nb >> 1) * 128;
+          *(uint16_t*)wp = (uint16_t)p;
+          *(uint16_t*)(wp + 256) = (uint16_t)(p >> 16);
+        }
       }
+      if (mb + 1 < G::MB) load_block(mb + 1, rot_c, scaled_c);  // next block's, while this one is stored
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's tile writes are done
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4_t v = *(const u32x4_t*)(((j & 1) ? rb1 : rb0) + j * 1024);
+        const int rl = wm * G::WROWS + mb * 32 + 4 * j + r4;
+        if (region == 0) {
+          // rows past M fall outside the descriptor and are dropped
+          __builtin_amdgcn_raw_buffer_store_b128(v, q_r, q_vo + (uint32_t)(mb * 32 + 4 * j) * (H * D * 2), 0, 0);
+        } else if (m0 + rl < M) {
+          const uint32_t slot = (uint32_t)s_slot[rl];
+          const uint64_t off = (uint64_t)(slot >> log2ps) * page_bytes +
+                               (((slot & (uint32_t)ps_mask) << 8) + kv_lane);
+          *(u32x4_t*)((char*)cache + off) = v;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // tile reads done before the next block's writes
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // tile reads done before the next block's writes
-  }
+  };
+  if (rot)
+    blocks(std::true_type{}, std::false_type{});  // row scale folded into the rotation table
+  else if (scaled)
+    blocks(std::false_type{}, std::true_type{});
+  else
+    blocks(std::false_type{}, std::false_type{});
 }
 
 // fp32: block = (token, region*H + head), D/2 threads, thread e computes the
@@ -266,7 +338,9 @@ extern "C" fc_status_t fc_rms_row_scale(const void* x, int32_t M, int32_t N, flo
 
 extern "C" size_t fc_qkv_workspace_size(int32_t T_q, int32_t head_dim, int32_t dtype) {
   if (dtype != FC_DTYPE_BF16 || T_q <= 0 || head_dim <= 0) return 0;
-  return (((size_t)T_q * (head_dim / 2) * sizeof(float2)) + 255) / 256 * 256;
+  // rotation table, then one cache slot per token
+  return (((size_t)T_q * (head_dim / 2) * sizeof(float2) + (size_t)T_q * sizeof(int32_t)) + 255) /
+         256 * 256;
 }
 
 extern "C" fc_status_t fc_qkv_rope_cache_write(
@@ -320,16 +394,17 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
     const int bm = gemm8_pick_bm(T_q, n_tiles_n);
     const int n_tiles_m = (T_q + bm - 1) / bm;
     const int n_rot = T_q * (head_dim / 2);
-    hipLaunchKernelGGL(rope_table_kernel, dim3((n_rot + 255) / 256), dim3(256), 0, st, positions,
-                       T_q, head_dim / 2, rope_base, (float2*)workspace);
-#define FC_QKV_LAUNCH(BMV)                                                                      \
-    hipLaunchKernelGGL(qkv_rope_cache_bf16_d128<BMV>, dim3(n_tiles_m * n_tiles_n), dim3(512), 0, \
-                       st, (const uint16_t*)hidden, positions, cu_seqlens_q, B, T_q,              \
-                       (const uint16_t*)w_qkv, d_model, n_heads, rope_base, (uint16_t*)k_cache,   \
-                       (uint16_t*)v_cache, block_table, max_pages_per_seq, log2ps,                \
-                       (uint16_t*)q_out, slot_mapping, (const float2*)workspace, row_scale,       \
-                       n_tiles_n)
-    if (bm == 128) FC_QKV_LAUNCH(128); else FC_QKV_LAUNCH(256);
+    float2* rope_tab = (float2*)workspace;
+    int32_t* slots = block_table ? (int32_t*)(rope_tab + n_rot) : nullptr;
+    hipLaunchKernelGGL(qkv_prepass_kernel, dim3((n_rot + 255) / 256), dim3(256), 0, st, positions,
+                       T_q, head_dim / 2, rope_base, rope_tab, cu_seqlens_q, B, block_table,
+                       max_pages_per_seq, log2ps, slots, slot_mapping, row_scale);
+#define FC_QKV_LAUNCH(GT)                                                                       \
+    hipLaunchKernelGGL(qkv_rope_cache_bf16_d128<GT>, dim3(n_tiles_m * n_tiles_n), dim3(GT::THREADS), \
+                       0, st, (const uint16_t*)hidden, T_q, (const uint16_t*)w_qkv, d_model,     \
+                       n_heads, (uint16_t*)k_cache, (uint16_t*)v_cache, slots, log2ps,            \
+                       (uint16_t*)q_out, rope_tab, row_scale, n_tiles_n)
+    if (bm == 128) FC_QKV_LAUNCH(Gemm8<128>); else FC_QKV_LAUNCH(Gemm8<256>);
 #undef FC_QKV_LAUNCH
     return fc_check_launch("fc_qkv_rope_cache_write");
   }
