@@ -149,7 +149,10 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
   // wave-private 8 KB LDS tile (32 rows of 256 bytes; rows with bit 2 set swap
   // their 64-byte halves, so the two row groups of a write phase fall on
   // different banks), then 16-byte row chunks out, 16 lanes per row: every
-  // store writes whole 128-byte lines.
+  // store writes whole 128-byte lines. The stores are nontemporal (sc0 nt): the
+  // outputs are not read again by this kernel, and every workgroup writes its
+  // 128 KB at about the same time, which would otherwise push the operand
+  // slices out of L2 (1-1.5 % faster in A/B runs).
   // (8 waves of a 128-row tile: the second stage holds waves 0-5, the third one waves 6 and 7)
   constexpr bool one_stage = G::STAGE >= (G::THREADS / 64) * 32 * 256;
   char* tile = (one_stage || wave < 6) ? st1 + wave * (32 * 256) : st2 + (wave - 6) * (32 * 256);
@@ -219,12 +222,12 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
         const int rl = wm * G::WROWS + mb * 32 + 4 * j + r4;
         if (region == 0) {
           // rows past M fall outside the descriptor and are dropped
-          __builtin_amdgcn_raw_buffer_store_b128(v, q_r, q_vo + (uint32_t)(mb * 32 + 4 * j) * (H * D * 2), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, q_r, q_vo + (uint32_t)(mb * 32 + 4 * j) * (H * D * 2), 0, 3);
         } else if (m0 + rl < M) {
           const uint32_t slot = (uint32_t)s_slot[rl];
           const uint64_t off = (uint64_t)(slot >> log2ps) * page_bytes +
                                (((slot & (uint32_t)ps_mask) << 8) + kv_lane);
-          *(u32x4_t*)((char*)cache + off) = v;
+          __builtin_nontemporal_store(v, (u32x4_t*)((char*)cache + off));
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // tile reads done before the next block's writes
