@@ -265,6 +265,65 @@ def test_topk_kernel_planted_ties(torch_cuda):
                                                                         nan=-1)), f"k={k} scores"
 
 
+@pytest.mark.parametrize("T", [200, 3000])
+def test_qkv_row_scale_both_tile_heights(torch_cuda, T):
+    """Projection of RMS-normalised inputs (the layer stack's use: a per-row scale
+    from fc_rms_row_scale, folded into the rotation table for Q and K and applied
+    to V) at a row count that takes the 128-row tile (T=200) and one that takes
+    the 256-row tile (T=3000); sampled rows against the oracle's normalised
+    projection, cache slots bit-exact, untouched cache rows unchanged."""
+    torch = torch_cuda
+    from kv_cache_attention_step_amd import flashcache as fc
+    from kv_cache_attention_step_amd.runner import to_device, to_host
+    _say(f"case qkv row scale T={T}")
+    H, D, ps, eps, base = 8, 128, 16, 1e-5, 5e5
+    d = H * D
+    rng = W.rng_for(77, T)
+    hid = W.to_bf16_bits((rng.standard_normal((T, d)) * 3.0).astype(np.float32))
+    w = W.to_bf16_bits((rng.standard_normal((3 * d, d)) * 0.02).astype(np.float32))
+    pos = rng.permutation(T + 40)[:T].astype(np.int32)   # distinct positions, one sequence
+    cu = np.array([0, T], np.int32)
+    maxp = (T + 40 + ps - 1) // ps
+    n_pages = maxp + 5
+    bt = rng.permutation(n_pages)[:maxp].astype(np.int32)[None, :]
+    kc0 = W.to_bf16_bits(rng.standard_normal((n_pages, H, ps, D)).astype(np.float32))
+    vc0 = W.to_bf16_bits(rng.standard_normal((n_pages, H, ps, D)).astype(np.float32))
+    g_hid, g_w, g_pos, g_cu, g_bt = (to_device(a) for a in (hid, w, pos, cu, bt))
+    g_kc, g_vc = to_device(kc0), to_device(vc0)
+    g_q = torch.empty((T, H, D), dtype=torch.int16, device="cuda")
+    g_sm = torch.empty(T, dtype=torch.int32, device="cuda")
+    g_rs = torch.empty(T, dtype=torch.float32, device="cuda")
+    wsb = fc.fc_qkv_workspace_size(T, D, fc.FC_DTYPE_BF16)
+    g_ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    fc.fc_rms_row_scale(g_hid.data_ptr(), T, d, eps, g_rs.data_ptr(), fc.FC_DTYPE_BF16)
+    fc.fc_qkv_rope_cache_write(g_hid.data_ptr(), g_pos.data_ptr(), g_cu.data_ptr(), 1, T,
+                               g_w.data_ptr(), d, H, D, base, g_kc.data_ptr(), g_vc.data_ptr(),
+                               g_bt.data_ptr(), maxp, ps, g_q.data_ptr(), g_sm.data_ptr(),
+                               g_ws.data_ptr(), wsb, fc.FC_DTYPE_BF16, row_scale=g_rs.data_ptr())
+    torch.cuda.synchronize()
+    q_out, sm = to_host(g_q), to_host(g_sm).astype(np.int64)
+    kc, vc = to_host(g_kc), to_host(g_vc)
+    # slots of every row (bit-exact), and no other cache row touched
+    slot_ref = bt[0, pos // ps].astype(np.int64) * ps + pos % ps
+    assert np.array_equal(sm, slot_ref), "slot mapping"
+    mask = np.ones(n_pages * ps, bool)
+    mask[slot_ref] = False
+    for got, ref, what in ((kc, kc0, "k"), (vc, vc0, "v")):
+        g = got.transpose(0, 2, 1, 3).reshape(-1, H, D)[mask]
+        r = ref.transpose(0, 2, 1, 3).reshape(-1, H, D)[mask]
+        assert np.array_equal(g, r), f"{what} cache: untouched slots changed"
+    # sampled rows (first, middle and last 16) against the oracle
+    rows = np.unique(np.concatenate([np.arange(16), T // 2 + np.arange(16), T - 16 + np.arange(16)]))
+    r = O.qkv_rope_cache_write(hid[rows], pos[rows], np.array([0, len(rows)]), w, H, D, base,
+                               kc0, vc0, bt, ps, "bf16", write_cache=False,
+                               rms_eps=eps)
+    assert np.array_equal(sm[rows], r["slot_mapping"]), "slot mapping (oracle)"
+    PU.assert_close(PU.as_f64(q_out[rows], "bf16"), r["q"], "bf16", "q rows")
+    pg, off = slot_ref[rows] // ps, slot_ref[rows] % ps
+    PU.assert_close(PU.as_f64(kc[pg, :, off, :], "bf16"), r["k"], "bf16", "k rows")
+    PU.assert_close(PU.as_f64(vc[pg, :, off, :], "bf16"), r["v"], "bf16", "v rows")
+
+
 @pytest.mark.parametrize("M,N,K", [
     (300, 512, 1024),     # 128-row DMA tiles, ragged last row tile
     (1100, 12288, 256),   # 256-row DMA tiles (enough column tiles to fill the CUs)
