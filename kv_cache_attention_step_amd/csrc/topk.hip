@@ -85,12 +85,20 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
   }
 
   // 1. head-summed scores (heads added in ascending order) and candidate flags;
-  //    eight loads are issued before their additions
+  //    up to 32 loads are issued before their additions (one memory latency per
+  //    key for up to 32 heads)
   int my_cand = 0;
   for (int j = t; j < L; j += TK_THREADS) {
     const float* src = imp + k0 + j;
     float s = 0.f;
     int h = 0;
+    for (; h + 32 <= H; h += 32) {
+      float x[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) x[u] = src[(size_t)(h + u) * T_k];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) s += x[u];
+    }
     for (; h + 8 <= H; h += 8) {
       float x[8];
 #pragma unroll
@@ -121,14 +129,33 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         if ((key & prefix_mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1);
       }
       __syncthreads();
-      // bins from the top: cum = number of keys in bins >= 255 - t; the chosen
-      // bin is the first (highest) one where cum reaches `need`
-      const int hcount = t < 256 ? s_hist[255 - t] : 0;
-      int below;
-      block_exclusive_scan(hcount, s_scan, &below);
-      if (t < 256 && below < need && below + hcount >= need) {
-        s_ctl[0] = 255 - t;
-        s_ctl[1] = need - below;
+      // bins from the top: the chosen bin is the first (highest) one where the
+      // count of keys in it and the bins above reaches `need`. One wave scans the
+      // 256 bins, four per lane (lane l: bins 255 - 4 l .. 252 - 4 l).
+      if (t < 64) {
+        int c4[4], tot = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          c4[u] = s_hist[255 - 4 * t - u];
+          tot += c4[u];
+        }
+        int incl = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off);
+          if (t >= off) incl += y;
+        }
+        int below = incl - tot;  // keys in the bins above this lane's four
+        if (below < need && incl >= need) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (below < need && below + c4[u] >= need) {
+              s_ctl[0] = 255 - 4 * t - u;
+              s_ctl[1] = need - below;
+            }
+            below += c4[u];
+          }
+        }
       }
       __syncthreads();
       prefix |= (uint32_t)s_ctl[0] << shift;
