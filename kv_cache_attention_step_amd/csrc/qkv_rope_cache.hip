@@ -74,17 +74,21 @@ __global__ void qkv_prepass_kernel(const int32_t* __restrict__ positions, int T,
   }
 }
 
-// bf16, D = 128: one workgroup per 256-wide column tile (two heads of one of
-// Q, K, V) of BM token rows, column tile fastest (consecutive workgroups, spread
-// over the XCDs round-robin, take different weight column blocks, so each XCD
-// streams a disjoint slice of W). The GEMM is one of the tile pipelines of
-// gemm_tile.hpp; a wave owns whole heads, so RoPE needs no exchange between lanes.
-template <class G>
+// bf16, D = 128: 256-wide column tiles (two heads of one of Q, K, V) of BM token
+// rows, column tile fastest (consecutive tiles, spread over the XCDs
+// round-robin, take different weight column blocks, so each XCD streams a
+// disjoint slice of W). The GEMM is one of the tile pipelines of gemm_tile.hpp;
+// a wave owns whole heads, so RoPE needs no exchange between lanes.
+// 128-row tiles: one workgroup per tile. 256-row tiles (PERSIST): one workgroup
+// per CU walks tiles blockIdx.x, + gridDim.x, ...; the next tile's first slice
+// is requested before this tile's epilogue, so its latency and the epilogue's
+// store burst overlap (about 1 % in A/B runs).
+template <class G, bool PERSIST>
 __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
     const uint16_t* __restrict__ hidden, int M, const uint16_t* __restrict__ w, int d, int H,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ slots,
     int log2ps, uint16_t* __restrict__ q_out, const float2* __restrict__ rope,
-    const float* __restrict__ row_scale, int n_tiles_n) {
+    const float* __restrict__ row_scale, int n_tiles_n, int n_tiles) {
   constexpr int BM = G::BM;
   constexpr int D = 128;
   // K-slice stages, kept as distinct objects (see Gemm8); the third is used by 128-row tiles only
@@ -92,25 +96,52 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
   __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[G::NST > 2 ? G::STAGE : 1024];
   char* const sts[3] = {st0, st1, st2};
+  static_assert(!PERSIST || (G::NST == 2 && G::STAGE >= (G::THREADS / 64) * 32 * 256),
+                "persistent tiles keep the epilogue in the second stage");
 
-  const int nt = blockIdx.x % n_tiles_n;
-  const int mt = blockIdx.x / n_tiles_n;
-  const int m0 = mt * BM, n0 = nt * QKV_BN;
   const int t = threadIdx.x;
-  // cache slot of tile row t (resolved by the pre-pass), requested before the
-  // main loop so its latency is hidden there
-  int slot_t = 0;
-  if (slots && t < BM && m0 + t < M) slot_t = slots[m0 + t];
-
-  f32x16_t acc[G::MB][G::NB];
-  G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, sts, acc);
-
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63, lr = lane & 31, h5 = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
+  const int c16 = (lane & 15) * 16, r4 = lane >> 4;
+  int tile = blockIdx.x;
+  if (PERSIST)
+    G::prologue(hidden, d, M, w, d, 3 * d, d, (tile / n_tiles_n) * BM, (tile % n_tiles_n) * QKV_BN,
+                sts);
+  for (;;) {
+  const int nt = tile % n_tiles_n;
+  const int mt = tile / n_tiles_n;
+  const int m0 = mt * BM, n0 = nt * QKV_BN;
   const int col0 = n0 + wn * D;  // first column of this wave's head
   const int region = col0 / d;   // 0 = Q, 1 = K, 2 = V
   const int h = (col0 - region * d) / D;
+  // Cache slots (resolved by the pre-pass), requested before the main loop so
+  // their latency is hidden there: one-shot tiles stage the slot of row t in
+  // LDS; persistent tiles (whose stages are busy with the next tile's first
+  // slice during the epilogue) keep the 16 rows this lane stores in registers.
+  int slot_t = 0;
+  int slot_r[PERSIST ? 2 * G::MB * 4 : 1];
+  if (!PERSIST) {
+    if (slots && t < BM && m0 + t < M) slot_t = slots[m0 + t];
+  } else if (region > 0) {
+#pragma unroll
+    for (int x = 0; x < G::MB * 8; ++x) {
+      const int row = min(m0 + wm * G::WROWS + (x >> 3) * 32 + 4 * (x & 7) + r4, M - 1);
+      slot_r[x] = slots[row];
+    }
+  }
+
+  f32x16_t acc[G::MB][G::NB];
+  if (PERSIST) {
+    G::template main_loop<true>(hidden, d, M, w, d, 3 * d, d, m0, n0, sts, acc);
+    const int next = tile + gridDim.x;
+    if (next < n_tiles)
+      G::prologue(hidden, d, M, w, d, 3 * d, d, (next / n_tiles_n) * BM,
+                  (next % n_tiles_n) * QKV_BN, sts);
+  } else {
+    G::run(hidden, d, M, w, d, 3 * d, d, m0, n0, sts, acc);
+  }
+
   const bool rot = region < 2;             // Q and K are rotated, V is not
   const bool scaled = row_scale != nullptr;
   const int row0 = m0 + wm * G::WROWS;     // first row of this wave
@@ -143,7 +174,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
       }
     }
   };
-  int* s_slot = (int*)st0;
+  int* s_slot = (int*)st0;  // one-shot tiles
 
   // Per 32-row block: RoPE or row scale in registers, bf16 values into a
   // wave-private 8 KB LDS tile (32 rows of 256 bytes; rows with bit 2 set swap
@@ -155,15 +186,14 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
   // slices out of L2 (1-1.5 % faster in A/B runs).
   // (8 waves of a 128-row tile: the second stage holds waves 0-5, the third one waves 6 and 7)
   constexpr bool one_stage = G::STAGE >= (G::THREADS / 64) * 32 * 256;
-  char* tile = (one_stage || wave < 6) ? st1 + wave * (32 * 256) : st2 + (wave - 6) * (32 * 256);
+  char* ep = (one_stage || wave < 6) ? st1 + wave * (32 * 256) : st2 + (wave - 6) * (32 * 256);
   // write side: row 8 (i / 4) + 4 h5 + i % 4, column nb * 32 + lr; the half
   // swap (bit 6 of the byte offset, set by h5) permutes the column blocks
-  char* const wb0 = tile + h5 * 1024 + lr * 2 + h5 * 64;         // blocks 0, 2
-  char* const wb1 = tile + h5 * 1024 + lr * 2 + 64 - h5 * 64;    // blocks 1, 3
+  char* const wb0 = ep + h5 * 1024 + lr * 2 + h5 * 64;         // blocks 0, 2
+  char* const wb1 = ep + h5 * 1024 + lr * 2 + 64 - h5 * 64;    // blocks 1, 3
   // read side: round j covers rows 4 j + lane / 16, chunk lane % 16 (swap on odd rounds)
-  const int c16 = (lane & 15) * 16, r4 = lane >> 4;
-  const char* const rb0 = tile + r4 * 256 + c16;
-  const char* const rb1 = tile + r4 * 256 + (c16 ^ 64);
+  const char* const rb0 = ep + r4 * 256 + c16;
+  const char* const rb1 = ep + r4 * 256 + (c16 ^ 64);
   uint16_t* cache = region == 1 ? kc : vc;
   const int ps_mask = (1 << log2ps) - 1;
   const __amdgpu_buffer_rsrc_t q_r = make_rsrc(q_out, (uint32_t)M * H * D * 2);
@@ -179,8 +209,10 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
   auto blocks = [&](auto rot_c, auto scaled_c) {
     constexpr bool ROT = decltype(rot_c)::value, SCALED = decltype(scaled_c)::value;
     load_block(0, rot_c, scaled_c);
-    if (t < BM) s_slot[t] = slot_t;
-    __syncthreads();
+    if (!PERSIST) {
+      if (t < BM) s_slot[t] = slot_t;
+      __syncthreads();
+    }
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb) {
       __builtin_amdgcn_sched_barrier(0);
@@ -224,7 +256,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
           // rows past M fall outside the descriptor and are dropped
           __builtin_amdgcn_raw_buffer_store_b128(v, q_r, q_vo + (uint32_t)(mb * 32 + 4 * j) * (H * D * 2), 0, 3);
         } else if (m0 + rl < M) {
-          const uint32_t slot = (uint32_t)s_slot[rl];
+          const uint32_t slot = (uint32_t)(PERSIST ? slot_r[mb * 8 + j] : s_slot[rl]);
           const uint64_t off = (uint64_t)(slot >> log2ps) * page_bytes +
                                (((slot & (uint32_t)ps_mask) << 8) + kv_lane);
           __builtin_nontemporal_store(v, (u32x4_t*)((char*)cache + off));
@@ -239,6 +271,10 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
     blocks(std::false_type{}, std::true_type{});
   else
     blocks(std::false_type{}, std::false_type{});
+  if (!PERSIST) break;
+  tile += gridDim.x;
+  if (tile >= n_tiles) break;
+  }
 }
 
 // fp32: block = (token, region*H + head), D/2 threads, thread e computes the
@@ -402,12 +438,18 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
     hipLaunchKernelGGL(qkv_prepass_kernel, dim3((n_rot + 255) / 256), dim3(256), 0, st, positions,
                        T_q, head_dim / 2, rope_base, rope_tab, cu_seqlens_q, B, block_table,
                        max_pages_per_seq, log2ps, slots, slot_mapping, row_scale);
-#define FC_QKV_LAUNCH(GT)                                                                       \
-    hipLaunchKernelGGL(qkv_rope_cache_bf16_d128<GT>, dim3(n_tiles_m * n_tiles_n), dim3(GT::THREADS), \
-                       0, st, (const uint16_t*)hidden, T_q, (const uint16_t*)w_qkv, d_model,     \
+    const int n_tiles = n_tiles_m * n_tiles_n;
+#define FC_QKV_LAUNCH(GT, PERS, GRID)                                                           \
+    hipLaunchKernelGGL((qkv_rope_cache_bf16_d128<GT, PERS>), dim3(GRID), dim3(GT::THREADS), 0,  \
+                       st, (const uint16_t*)hidden, T_q, (const uint16_t*)w_qkv, d_model,       \
                        n_heads, (uint16_t*)k_cache, (uint16_t*)v_cache, slots, log2ps,            \
-                       (uint16_t*)q_out, rope_tab, row_scale, n_tiles_n)
-    if (bm == 128) FC_QKV_LAUNCH(Gemm8<128>); else FC_QKV_LAUNCH(Gemm8<256>);
+                       (uint16_t*)q_out, rope_tab, row_scale, n_tiles_n, n_tiles)
+    if (bm == 128) {
+      FC_QKV_LAUNCH(Gemm8<128>, false, n_tiles);
+    } else {
+      const int grid = n_tiles < fc_num_cus() ? n_tiles : fc_num_cus();
+      FC_QKV_LAUNCH(Gemm8<256>, true, grid);
+    }
 #undef FC_QKV_LAUNCH
     return fc_check_launch("fc_qkv_rope_cache_write");
   }
