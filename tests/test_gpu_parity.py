@@ -233,14 +233,15 @@ def test_c2_deterministic(torch_cuda):
         assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
 
 
-def test_topk_kernel_planted_ties(torch_cuda):
+@pytest.mark.parametrize("H", [8, 32, 43])
+def test_topk_kernel_planted_ties(torch_cuda, H):
     """Importance built by the test with many exact ties: the kernel's selection
-    must equal the oracle's, both deciding on the same fp32 head-sum."""
+    must equal the oracle's, both deciding on the same fp32 head-sum. H = 8, 32
+    and 43 take the kernel's 8-, 32- and mixed head-load groups."""
     torch = torch_cuda
     from kv_cache_attention_step_amd import flashcache as fc
-    _say("case topk planted ties")
-    rng = np.random.default_rng(5)
-    H = 8
+    _say(f"case topk planted ties H={H}")
+    rng = np.random.default_rng(5 + H)
     lens = np.array([1, 7, 64, 300, 1537, 4096, 0, 33])
     B = len(lens)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -263,6 +264,35 @@ def test_topk_kernel_planted_ties(torch_cuda):
         gsc = sc.cpu().numpy()
         assert np.array_equal(np.nan_to_num(gsc, nan=-1), np.nan_to_num(osc.astype(np.float32),
                                                                         nan=-1)), f"k={k} scores"
+
+
+def test_topk_length_capacity(torch_cuda):
+    """A sequence of exactly FC_TOPK_MAX_LEN keys is selected like the oracle's; one
+    key more is reported as documented (count -1, positions -1, scores NaN) while
+    the other sequences of the same call are unaffected."""
+    torch = torch_cuda
+    from kv_cache_attention_step_amd import flashcache as fc
+    _say("case topk length capacity")
+    rng = np.random.default_rng(11)
+    H, k = 32, 48
+    lens = np.array([fc.FC_TOPK_MAX_LEN, fc.FC_TOPK_MAX_LEN + 1, 500])
+    B = len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T_k = int(cu[-1])
+    imp = rng.random((H, T_k)).astype(np.float32)
+    cand = (rng.random(T_k) < 0.5).astype(np.uint8)
+    pos = torch.full((B, k), 77, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, k), dtype=torch.float32, device="cuda")
+    fc.fc_importance_topk(torch.from_numpy(imp).cuda(), torch.from_numpy(cu).cuda(), B, T_k, H,
+                          torch.from_numpy(cand).cuda(), k, pos, cnt, sc)
+    torch.cuda.synchronize()
+    gpos, gcnt, gsc = pos.cpu().numpy(), cnt.cpu().numpy(), sc.cpu().numpy()
+    opos, ocnt, osc, _ = O.importance_topk(imp.astype(np.float64), cu, cand, k, score_float32=True)
+    for b in (0, 2):
+        assert gcnt[b] == ocnt[b] and np.array_equal(gpos[b], opos[b]), f"seq {b}"
+        assert np.array_equal(gsc[b], osc[b].astype(np.float32)), f"seq {b} scores"
+    assert gcnt[1] == -1 and np.all(gpos[1] == -1) and np.all(np.isnan(gsc[1])), "over-long sequence"
 
 
 @pytest.mark.parametrize("T", [200, 3000])
