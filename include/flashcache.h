@@ -110,9 +110,10 @@ const char* fc_version(void);
  *               hidden[t] * row_scale[t] (an input normalisation computed by
  *               fc_rms_row_scale)
  * workspace     device memory of at least fc_qkv_workspace_size() bytes (the
- *               per-token rotation table and cache slots; overwritten; NULL
- *               allowed when that size is 0; calls that overlap on one
- *               workspace race)
+ *               per-token rotation table and cache slots, and for bf16 calls
+ *               with few row tiles the fp32 partial products of a K-split
+ *               projection; overwritten; NULL allowed when that size is 0;
+ *               calls that overlap on one workspace race)
  * Supported: bf16 with D = 128 and d a multiple of 256; f32 with D in {64,128}.
  * page_size must be a power of two in [1, 256]. bf16: hidden, w_qkv, q_out,
  * k_cache, v_cache and workspace must be 16-byte aligned (FC_ERR_INVALID_VALUE
@@ -126,8 +127,10 @@ fc_status_t fc_qkv_rope_cache_write(
     const float* row_scale, void* workspace, size_t workspace_bytes, int32_t dtype,
     fc_stream_t stream);
 
-/* Bytes of device workspace fc_qkv_rope_cache_write needs (0 when none). */
-size_t fc_qkv_workspace_size(int32_t T_q, int32_t head_dim, int32_t dtype);
+/* Bytes of device workspace fc_qkv_rope_cache_write needs (0 when none). The
+ * K-split decision depends on the current device's compute-unit count, so query
+ * it with the device current that the call will run on. */
+size_t fc_qkv_workspace_size(int32_t T_q, int32_t d_model, int32_t head_dim, int32_t dtype);
 
 /* Bytes of device workspace fc_varlen_bidir_attention needs for these sizes
  * (0 when none). */

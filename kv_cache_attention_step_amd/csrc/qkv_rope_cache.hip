@@ -277,6 +277,82 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
   }
 }
 
+// Split-K for projections with few row tiles (one sequence: a 128-row tile
+// of 48 column tiles would use 48 of the CUs, each streaming 2 MB of weights):
+// split s of a 128 x 256 tile multiplies K range [s K / S, (s + 1) K / S) and
+// writes its fp32 partial tile to part[s][row][col]; qkv_splitk_epilogue adds
+// the S partials in split order (deterministic), then rotates, scales and
+// scatters like the one-pass epilogue.
+__global__ __launch_bounds__(512, 1) void qkv_splitk_partial(
+    const uint16_t* __restrict__ hidden, int M, const uint16_t* __restrict__ w, int d, int S,
+    int n_cols, float* __restrict__ part, int n_tiles_n) {
+  using G = Gemm8<128>;
+  __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[G::STAGE];
+  char* const sts[3] = {st0, st1, st2};
+  const int split = blockIdx.x % S;
+  const int tile = blockIdx.x / S;
+  const int nt = tile % n_tiles_n, mt = tile / n_tiles_n;
+  const int m0 = mt * G::BM, n0 = nt * QKV_BN;
+  const int kpart = d / S, k0 = split * kpart;
+  f32x16_t acc[G::MB][G::NB];
+  // operands from column k0 on: rows keep their full stride d
+  G::run(hidden + k0, d, M, w + k0, d, 3 * d, kpart, m0, n0, sts, acc);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  float* dst = part + (size_t)split * M * n_cols;
+#pragma unroll
+  for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = m0 + wm * G::WROWS + acc_row(0, i, lane);
+      if (row < M) dst[(size_t)row * n_cols + n0 + wn * 128 + acc_col(nb, lane)] = acc[0][nb][i];
+    }
+}
+
+// One workgroup per (token, region * H + head), 64 threads: thread e owns the
+// rotation pair (e, e + 64) of that head.
+__global__ __launch_bounds__(64) void qkv_splitk_epilogue(
+    const float* __restrict__ part, int S, int M, int n_cols, int d, int H,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ slots,
+    int log2ps, uint16_t* __restrict__ q_out, const float2* __restrict__ rope,
+    const float* __restrict__ row_scale) {
+  constexpr int D = 128;
+  const int row = blockIdx.x;
+  const int region = blockIdx.y / H, h = blockIdx.y % H;
+  const int e = threadIdx.x;
+  const size_t c0 = (size_t)region * d + h * D + e;
+  float x = 0.f, y = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    const float* src = part + ((size_t)sp * M + row) * n_cols + c0;
+    x += src[0];
+    y += src[D / 2];
+  }
+  if (region < 2) {
+    // pair e sits at entry 2 (e mod 32) + e div 32 of the token's table (r folded in)
+    const float2 cs = rope[(size_t)row * (D / 2) + 2 * (e & 31) + (e >> 5)];
+    const float a = x * cs.x - y * cs.y, b = y * cs.x + x * cs.y;
+    x = a;
+    y = b;
+  } else if (row_scale) {
+    const float r = row_scale[row];
+    x *= r;
+    y *= r;
+  }
+  uint16_t* dst;
+  if (region == 0) {
+    dst = q_out + ((size_t)row * H + h) * D;
+  } else {
+    const int slot = slots[row];
+    const int ps_mask = (1 << log2ps) - 1;
+    dst = (region == 1 ? kc : vc) + (((size_t)(slot >> log2ps) * H + h) * (ps_mask + 1) + (slot & ps_mask)) * D;
+  }
+  dst[e] = f32_to_bf16(x);
+  dst[e + D / 2] = f32_to_bf16(y);
+}
+
 // fp32: block = (token, region*H + head), D/2 threads, thread e computes the
 // rotation pair (e, e + D/2) of its head.
 __global__ void qkv_rope_cache_f32(const float* __restrict__ hidden,
@@ -375,11 +451,28 @@ extern "C" fc_status_t fc_rms_row_scale(const void* x, int32_t M, int32_t N, flo
   return fc_check_launch("fc_rms_row_scale");
 }
 
-extern "C" size_t fc_qkv_workspace_size(int32_t T_q, int32_t head_dim, int32_t dtype) {
-  if (dtype != FC_DTYPE_BF16 || T_q <= 0 || head_dim <= 0) return 0;
-  // rotation table, then one cache slot per token
-  return (((size_t)T_q * (head_dim / 2) * sizeof(float2) + (size_t)T_q * sizeof(int32_t)) + 255) /
-         256 * 256;
+// K splits of the bf16 projection with the cache write: 4 when even its
+// 128-row tiles would fill at most a quarter of the CUs (T_q up to
+// qkv_split_rows_max: 128 rows at d = 4096 on 256 CUs); else 1.
+constexpr int QKV_KSPLIT = 4;  // 2: 69 us, 4: 58 us, 8: 69 us at 128 rows x d 4096
+static int qkv_split_rows_max(int d_model) {
+  const int tn = 3 * d_model / QKV_BN;
+  return tn > 0 ? 128 * (fc_num_cus() / (4 * tn)) : 0;
+}
+static int qkv_k_splits(int T_q, int d_model, bool write_cache) {
+  return (write_cache && T_q <= qkv_split_rows_max(d_model)) ? QKV_KSPLIT : 1;
+}
+
+extern "C" size_t fc_qkv_workspace_size(int32_t T_q, int32_t d_model, int32_t head_dim,
+                                        int32_t dtype) {
+  if (dtype != FC_DTYPE_BF16 || T_q <= 0 || head_dim <= 0 || d_model <= 0) return 0;
+  // rotation table, one cache slot per token, then the fp32 partial products
+  // of a K-split projection for up to qkv_split_rows_max rows (so the size
+  // never shrinks as T_q grows: a buffer sized for the largest T_q serves all)
+  const size_t head = ((size_t)T_q * (head_dim / 2) * sizeof(float2) + (size_t)T_q * sizeof(int32_t) +
+                       255) / 256 * 256;
+  const int split_rows = T_q < qkv_split_rows_max(d_model) ? T_q : qkv_split_rows_max(d_model);
+  return head + (size_t)QKV_KSPLIT * split_rows * 3 * d_model * sizeof(float);
 }
 
 extern "C" fc_status_t fc_qkv_rope_cache_write(
@@ -421,9 +514,9 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
     FC_REQUIRE((int64_t)T_q * d_model * 2 < (1ll << 31) &&
                    (int64_t)3 * d_model * d_model * 2 < (1ll << 31),
                FC_ERR_UNSUPPORTED, "fc_qkv_rope_cache_write: operands above 2 GiB");
-    FC_REQUIRE(workspace && workspace_bytes >= fc_qkv_workspace_size(T_q, head_dim, dtype),
+    FC_REQUIRE(workspace && workspace_bytes >= fc_qkv_workspace_size(T_q, d_model, head_dim, dtype),
                FC_ERR_WORKSPACE, "fc_qkv_rope_cache_write: workspace of %zu bytes required",
-               fc_qkv_workspace_size(T_q, head_dim, dtype));
+               fc_qkv_workspace_size(T_q, d_model, head_dim, dtype));
     // 16-byte loads and stores of rows
     const uintptr_t mis = (uintptr_t)hidden | (uintptr_t)w_qkv | (uintptr_t)q_out |
                           (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)workspace;
@@ -439,6 +532,20 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
                        T_q, head_dim / 2, rope_base, rope_tab, cu_seqlens_q, B, block_table,
                        max_pages_per_seq, log2ps, slots, slot_mapping, row_scale);
     const int n_tiles = n_tiles_m * n_tiles_n;
+    const int n_cols = write_cache ? 3 * d_model : d_model;
+    const int S = qkv_k_splits(T_q, d_model, write_cache);
+    if (S > 1) {
+      float* part = (float*)((char*)workspace + ((size_t)n_rot * sizeof(float2) +
+                                                 (size_t)T_q * sizeof(int32_t) + 255) / 256 * 256);
+      const int tn = n_cols / QKV_BN, tm = (T_q + 127) / 128;
+      hipLaunchKernelGGL(qkv_splitk_partial, dim3(tm * tn * S), dim3(512), 0, st,
+                         (const uint16_t*)hidden, T_q, (const uint16_t*)w_qkv, d_model, S, n_cols,
+                         part, tn);
+      hipLaunchKernelGGL(qkv_splitk_epilogue, dim3(T_q, n_cols / head_dim), dim3(64), 0, st, part,
+                         S, T_q, n_cols, d_model, n_heads, (uint16_t*)k_cache, (uint16_t*)v_cache,
+                         slots, log2ps, (uint16_t*)q_out, rope_tab, row_scale);
+      return fc_check_launch("fc_qkv_rope_cache_write");
+    }
 #define FC_QKV_LAUNCH(GT, PERS, GRID)                                                           \
     hipLaunchKernelGGL((qkv_rope_cache_bf16_d128<GT, PERS>), dim3(GRID), dim3(GT::THREADS), 0,  \
                        st, (const uint16_t*)hidden, T_q, (const uint16_t*)w_qkv, d_model,       \

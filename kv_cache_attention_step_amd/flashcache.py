@@ -49,7 +49,7 @@ _SIGS = {
     "fc_qkv_rope_cache_write": ([P, P, P, I32, I32, P, I32, I32, I32, F32, P, P, P, I32, I32, P, P,
                                  P, P, SZ, I32, P], I32),
     "fc_rms_row_scale": ([P, I32, I32, F32, P, I32, P], I32),
-    "fc_qkv_workspace_size": ([I32, I32, I32], SZ),
+    "fc_qkv_workspace_size": ([I32, I32, I32, I32], SZ),
     "fc_attention_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
     "fc_varlen_bidir_attention": ([P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, F32, P, P,
                                    I32, P, SZ, I32, P], I32),
@@ -106,8 +106,8 @@ def fc_status_string(status: int) -> str:
     return load().fc_status_string(status).decode()
 
 
-def fc_qkv_workspace_size(T_q, head_dim, dtype) -> int:
-    return int(load().fc_qkv_workspace_size(T_q, head_dim, dtype))
+def fc_qkv_workspace_size(T_q, d_model, head_dim, dtype) -> int:
+    return int(load().fc_qkv_workspace_size(T_q, d_model, head_dim, dtype))
 
 
 def fc_qkv_rope_cache_write(hidden, positions, cu_seqlens_q, B, T_q, w_qkv, d_model, n_heads,

@@ -84,7 +84,7 @@ class StepBuffers:
         ws = fc.fc_attention_workspace_size(self.B, self.T_q, self.T_k, self.H, self.D, 1)
         self.ws_bytes = ws
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws else None
-        qws = fc.fc_qkv_workspace_size(self.T_q, self.D, self.dtype)
+        qws = fc.fc_qkv_workspace_size(self.T_q, self.H * self.D, self.D, self.dtype)
         self.qkv_ws_bytes = qws
         self.qkv_workspace = torch.empty(qws, dtype=torch.uint8, device=device) if qws else None
         self.max_seqlen_q = inp.max_seqlen_q
@@ -241,7 +241,7 @@ class LayerStackDriver:
         ws = fc.fc_attention_workspace_size(self.B, T_max, self.T_k, self.H, self.D, 1)
         self.ws_bytes = ws
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
-        qws = fc.fc_qkv_workspace_size(T_max, self.D, self.dtype)
+        qws = fc.fc_qkv_workspace_size(T_max, self.H * self.D, self.D, self.dtype)
         self.qkv_ws_bytes = qws
         self.qkv_workspace = torch.empty(max(qws, 1), dtype=torch.uint8, device=device)
         self.scale = 1.0 / math.sqrt(self.D)

@@ -84,7 +84,7 @@ def test_qkv_argument_checks():
     expect("FC_ERR_UNSUPPORTED", n_heads=4, head_dim=64)    # bf16 supports D = 128 only
     expect("FC_ERR_UNSUPPORTED", n_heads=3, d_model=384)    # d % 256 != 0
     expect("FC_ERR_UNSUPPORTED", dtype=fc.FC_DTYPE_F32, n_heads=8, head_dim=32)
-    need = fc.fc_qkv_workspace_size(4, 128, fc.FC_DTYPE_BF16)
+    need = fc.fc_qkv_workspace_size(4, 256, 128, fc.FC_DTYPE_BF16)
     assert need >= 4 * 64 * 8
     expect("FC_ERR_WORKSPACE", workspace_bytes=need - 1)
     expect("FC_ERR_WORKSPACE", workspace=None)
@@ -93,7 +93,7 @@ def test_qkv_argument_checks():
         if name == "k_cache":
             over["v_cache"] = FAKE + 8
         expect("FC_ERR_INVALID_VALUE", **over)
-    assert fc.fc_qkv_workspace_size(4, 64, fc.FC_DTYPE_F32) == 0
+    assert fc.fc_qkv_workspace_size(4, 256, 64, fc.FC_DTYPE_F32) == 0
     # nothing to do is not an error
     call(T_q=0)(0)
 

@@ -323,7 +323,7 @@ def test_qkv_row_scale_both_tile_heights(torch_cuda, T):
     g_q = torch.empty((T, H, D), dtype=torch.int16, device="cuda")
     g_sm = torch.empty(T, dtype=torch.int32, device="cuda")
     g_rs = torch.empty(T, dtype=torch.float32, device="cuda")
-    wsb = fc.fc_qkv_workspace_size(T, D, fc.FC_DTYPE_BF16)
+    wsb = fc.fc_qkv_workspace_size(T, d, D, fc.FC_DTYPE_BF16)
     g_ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     fc.fc_rms_row_scale(g_hid.data_ptr(), T, d, eps, g_rs.data_ptr(), fc.FC_DTYPE_BF16)
     fc.fc_qkv_rope_cache_write(g_hid.data_ptr(), g_pos.data_ptr(), g_cu.data_ptr(), 1, T,
