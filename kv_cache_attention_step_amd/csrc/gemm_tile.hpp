@@ -229,15 +229,6 @@ struct Gemm8 {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // K must be a multiple of 64. st[0 .. NST-1]: distinct __shared__ arrays of
-  // STAGE bytes (distinct objects, so the compiler sees that fragment reads of
-  // one stage do not depend on loads landing in another and adds no wait of its
-  // own); slice s lives in stage s mod NST and is requested NST - 1 slices ahead.
-  // The slice count is padded to a multiple of NST: past the last slice the
-  // loads go through a zero-range buffer descriptor (no memory access) and the
-  // MFMAs are skipped, so every slice issues the same loads and the wait counts
-  // are constants. Ends with every load landed and a barrier, so the caller may
-  // reuse the stages.
   // Requests the first NST - 1 slices (the part of run() that may be issued
   // early, e.g. before the previous tile's epilogue).
   static FC_DEVICE void prologue(const uint16_t* __restrict__ A, int lda, int M,
@@ -256,6 +247,16 @@ struct Gemm8 {
     }
   }
 
+  // acc = A[m0 .., 0 .. K) . Bm[n0 .., 0 .. K)^T for the tile; rows past M or N
+  // read as 0. K must be a multiple of 64. st[0 .. NST-1]: distinct __shared__
+  // arrays of STAGE bytes (distinct objects, so the compiler sees that fragment
+  // reads of one stage do not depend on loads landing in another and adds no
+  // wait of its own); slice s lives in stage s mod NST and is requested NST - 1
+  // slices ahead. The slice count is padded to a multiple of NST: past the last
+  // slice the loads go through a zero-range buffer descriptor (no memory access)
+  // and the MFMAs are skipped, so every slice issues the same loads and the wait
+  // counts are constants. Ends with every load landed and a barrier, so the
+  // caller may reuse the stages.
   static FC_DEVICE void run(const uint16_t* __restrict__ A, int lda, int M,
                             const uint16_t* __restrict__ Bm, int ldb, int N, int K, int m0, int n0,
                             char* const (&st)[3], f32x16_t (&acc)[MB][NB]) {
