@@ -580,6 +580,172 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
   }
 }
 
+// ---- key split for few (sequence, head) items (importance path) -------------
+// With few items (one sequence: 32) one workgroup per item would use a few of
+// the CUs, so each item's key tiles are split into S chunks of ct tiles and the
+// two passes become three launches: attn_split_stats (row max and normaliser
+// of each chunk), attn_split_main (every chunk combines the S partial
+// statistics of its rows in chunk order, then forms P over its keys, writes
+// their column sums and its normalised O partial) and attn_split_reduce (O =
+// sum of the partials in chunk order). Query rows per item: at most 128 (4
+// waves x 32 rows, rows past Q zero-filled). Deterministic.
+struct SplitArgs {
+  int S;             // chunks per item (chunk c: tiles c ct .. c ct + ct - 1, ct = ceil(tiles / S))
+  float2* stats;     // [items][S][128] (m, l) in the log2 domain of the kernel
+  float* opart;      // [items][S][128][128] normalised O partials
+};
+
+template <bool PS_GE16>
+__global__ __launch_bounds__(256, 2) void attn_split_stats(AttnArgs a, SplitArgs sp) {
+  __shared__ __attribute__((aligned(16))) char lds[A_LDS];
+  const int item = blockIdx.x / sp.S, chunk = blockIdx.x % sp.S;
+  const int b = item / a.H, h = item % a.H;
+  const int q0 = a.cu_q[b], Q = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], L = a.cu_k[b + 1] - k0;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int32_t* bt = a.block_table + (size_t)b * a.maxp;
+  const int n_tiles = (L + AKT - 1) / AKT;
+  const int ct = (n_tiles + sp.S - 1) / sp.S;
+  const int t0 = min(n_tiles, chunk * ct), t1 = min(n_tiles, t0 + ct);
+  const bool ragged = (L & (AKT - 1)) != 0;
+  const float c = a.scale_log2;
+  const int row = wave * 32 + (lane & 31);
+  float m = -INFINITY, l = 0.f;
+  if (Q > 0 && t0 < t1) {
+    bf16x8_t qf[8];
+    load_q(a, q0, row, Q, h, qf);
+    TileRegs tr;
+    load_group<PS_GE16, false>(a, bt, h, t0, L, wave, lane, tr);
+    store_group<false>(lds, wave, lane, tr);
+    __syncthreads();
+    for (int tile = t0; tile < t1; ++tile) {
+      const bool last = tile + 1 == n_tiles;
+      load_group<PS_GE16, false>(a, bt, h, tile + 1, L, wave, lane, tr);
+      const char* ks = lds + ((tile - t0) & 1) * A_STAGE;
+      f32x16_t s0 = s_block(ks, 0, qf, lane);
+      f32x16_t s1 = s_block(ks, 1, qf, lane);
+      if (ragged && last) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (tile * AKT + s_key(0, i, lane) >= L) s0[i] = -INFINITY;
+          if (tile * AKT + s_key(1, i, lane) >= L) s1[i] = -INFINITY;
+        }
+      }
+      float tmax = s0[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s0[i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
+      const float mn = fmaxf(m, tmax * c);
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += fexp2(fmaf(s0[i], c, -mref));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += fexp2(fmaf(s1[i], c, -mref));
+      l = (m == -INFINITY ? 0.f : l * fexp2(m - mn)) + sum;
+      m = mn;
+      store_group<false>(lds + ((tile - t0 + 1) & 1) * A_STAGE, wave, lane, tr);
+      __syncthreads();
+    }
+  }
+  const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
+  const float mf = fmaxf(m, mo);
+  const float lf = (m == -INFINITY ? 0.f : l * fexp2(m - mf)) + (mo == -INFINITY ? 0.f : lo * fexp2(mo - mf));
+  if (lane < 32) sp.stats[((size_t)item * sp.S + chunk) * AROWS + row] = make_float2(mf, lf);
+}
+
+template <bool PS_GE16>
+__global__ __launch_bounds__(256, 2) void attn_split_main(AttnArgs a, SplitArgs sp) {
+  __shared__ __attribute__((aligned(16))) char lds[A_LDS];
+  float* red = (float*)(lds + 2 * A_STAGE);
+  const int item = blockIdx.x / sp.S, chunk = blockIdx.x % sp.S;
+  const int b = item / a.H, h = item % a.H;
+  const int q0 = a.cu_q[b], Q = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], L = a.cu_k[b + 1] - k0;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int32_t* bt = a.block_table + (size_t)b * a.maxp;
+  const int n_tiles = (L + AKT - 1) / AKT;
+  const int ct = (n_tiles + sp.S - 1) / sp.S;
+  const int t0 = min(n_tiles, chunk * ct), t1 = min(n_tiles, t0 + ct);
+  const float c = a.scale_log2;
+  const int row = wave * 32 + (lane & 31);
+  const bool row_ok = row < Q;
+  float* op = sp.opart + (((size_t)item * sp.S + chunk) * AROWS + row) * AD + (lane >> 5) * 4;
+  f32x16_t o[4] = {};
+  if (Q == 0) {  // no query rows: column sums are 0
+    if (!a.accumulate)
+      for (int key = t0 * AKT + t; key < min(L, t1 * AKT); key += blockDim.x)
+        a.imp[(size_t)h * a.T_k + k0 + key] = 0.f;
+  } else if (t0 < t1) {
+    // statistics of the whole row, combined over the chunks in chunk order
+    float mf = -INFINITY, lf = 0.f;
+    for (int ch = 0; ch < sp.S; ++ch) {
+      const float2 st = sp.stats[((size_t)item * sp.S + ch) * AROWS + row];
+      const float mx = fmaxf(mf, st.x);
+      lf = (mf == -INFINITY ? 0.f : lf * fexp2(mf - mx)) + (st.x == -INFINITY ? 0.f : st.y * fexp2(st.x - mx));
+      mf = mx;
+    }
+    const float off = row_ok ? mf + __builtin_amdgcn_logf(lf) : INFINITY;
+    bf16x8_t qf[8];
+    load_q(a, q0, row, Q, h, qf);
+    TileRegs tr;
+    load_group<PS_GE16, true>(a, bt, h, t0, L, wave, lane, tr);
+    store_group<true>(lds, wave, lane, tr);
+    __syncthreads();
+    for (int tile = t0; tile < t1; ++tile) {
+      load_group<PS_GE16, true>(a, bt, h, tile + 1, L, wave, lane, tr);
+      const char* ks = lds + ((tile - t0) & 1) * A_STAGE;
+      const char* vs = ks + K_TILE;
+      float* rb = red + ((tile - t0) & 1) * 4 * AKT;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16_t s = s_block(ks, kb, qf, lane);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = fexp2(fmaf(s[i], c, -off));
+        // keys past L were loaded as zero K and V rows: their P multiplies zero
+        // V rows and their column sums are never stored
+        pv_chunk(vs, kb, 0, s, o, lane);
+        pv_chunk(vs, kb, 1, s, o, lane);
+        const float colsum = transpose_reduce16(s, lane);
+        if ((lane & 1) == 0) rb[wave * AKT + reduced_key(kb, lane)] = colsum;
+      }
+      store_group<true>(lds + ((tile - t0 + 1) & 1) * A_STAGE, wave, lane, tr);
+      __syncthreads();
+      if (t < AKT) {
+        const int key = tile * AKT + t;
+        if (key < L) {
+          const float v = rb[t] + rb[AKT + t] + rb[2 * AKT + t] + rb[3 * AKT + t];
+          float* dst = a.imp + (size_t)h * a.T_k + k0 + key;
+          *dst = a.accumulate ? *dst + v : v;
+        }
+      }
+    }
+  }
+  // normalised O partial of this chunk (0 for an empty chunk), in the layout
+  // of store_o: dims db * 32 + g * 8 + (lane / 32) * 4 + j of row `row`
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(float4*)(op + db * 32 + g * 8) =
+          make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+}
+
+// out[q0 + row, h, :] = bf16(sum over chunks of the O partials), rows < Q.
+__global__ __launch_bounds__(AD) void attn_split_reduce(AttnArgs a, SplitArgs sp) {
+  const int item = blockIdx.x / AROWS, row = blockIdx.x % AROWS;
+  const int b = item / a.H, h = item % a.H;
+  const int q0 = a.cu_q[b], Q = a.cu_q[b + 1] - q0;
+  if (row >= Q) return;
+  const int dim = threadIdx.x;
+  float acc = 0.f;
+  for (int ch = 0; ch < sp.S; ++ch) acc += sp.opart[(((size_t)item * sp.S + ch) * AROWS + row) * AD + dim];
+  a.out[((size_t)(q0 + row) * a.H + h) * AD + dim] = f32_to_bf16(acc);
+}
+
 // Longest-processing-time-first order of the sequences (by cache length; equal
 // lengths keep their index order), so the long (sequence, head) items start first.
 __global__ void lpt_order(const int32_t* __restrict__ cu_k, int B, int32_t* __restrict__ order) {
@@ -681,11 +847,26 @@ __global__ __launch_bounds__(64) void attn_f32(const float* __restrict__ q,
 
 }  // namespace
 
+// Key split (importance path, bf16, at most 128 query rows per sequence): when
+// the (sequence, head) items would occupy at most a quarter of the CUs, each
+// item's keys go to S = min(8, CUs / items) chunks.
+static int attn_key_splits(int B, int n_heads) {
+  const int items = B * n_heads, n_cu = fc_num_cus();
+  if (items <= 0 || items * 4 > n_cu) return 1;
+  return n_cu / items < 8 ? n_cu / items : 8;
+}
+
 extern "C" size_t fc_attention_workspace_size(int32_t B, int32_t T_q, int32_t T_k, int32_t n_heads,
                                               int32_t head_dim, int32_t with_importance) {
-  (void)T_q; (void)T_k; (void)n_heads; (void)head_dim; (void)with_importance;
-  // the longest-first sequence order
-  return B > 0 ? (((size_t)B * sizeof(int32_t) + 255) / 256) * 256 : 0;
+  (void)T_q; (void)T_k;
+  if (B <= 0) return 0;
+  // the longest-first sequence order, then (key split) the chunk statistics
+  // and O partials
+  size_t bytes = (((size_t)B * sizeof(int32_t) + 255) / 256) * 256;
+  const int S = (with_importance && head_dim == AD) ? attn_key_splits(B, n_heads) : 1;
+  if (S > 1)
+    bytes += (size_t)B * n_heads * S * AROWS * (sizeof(float2) + AD * sizeof(float));
+  return bytes;
 }
 
 extern "C" fc_status_t fc_varlen_bidir_attention(
@@ -744,6 +925,24 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
     else
       hipLaunchKernelGGL(lpt_order, dim3(1), dim3(256), 0, st, cu_seqlens_k, B, (int32_t*)workspace);
     const bool ps16 = page_size >= 16;
+    const int S = importance ? attn_key_splits(B, n_heads) : 1;
+    if (S > 1 && max_seqlen_q <= AROWS && ((uintptr_t)workspace & 15) == 0) {
+      SplitArgs sp;
+      sp.S = S;
+      char* ws = (char*)workspace + (((size_t)B * sizeof(int32_t) + 255) / 256) * 256;
+      sp.stats = (float2*)ws;
+      sp.opart = (float*)(ws + (size_t)B * n_heads * S * AROWS * sizeof(float2));
+      const dim3 g(B * n_heads * S);
+      if (ps16) {
+        hipLaunchKernelGGL(attn_split_stats<true>, g, dim3(256), 0, st, a, sp);
+        hipLaunchKernelGGL(attn_split_main<true>, g, dim3(256), 0, st, a, sp);
+      } else {
+        hipLaunchKernelGGL(attn_split_stats<false>, g, dim3(256), 0, st, a, sp);
+        hipLaunchKernelGGL(attn_split_main<false>, g, dim3(256), 0, st, a, sp);
+      }
+      hipLaunchKernelGGL(attn_split_reduce, dim3(B * n_heads * AROWS), dim3(AD), 0, st, a, sp);
+      return fc_check_launch("fc_varlen_bidir_attention");
+    }
     // one-pass: (sequence, head) items in groups of 8, one per XCD, each group's
     // row tiles consecutive per XCD (see the kernel's block mapping)
     const dim3 grid(importance ? B * n_heads : ((B * n_heads + 7) / 8) * 8 * a.n_rt);

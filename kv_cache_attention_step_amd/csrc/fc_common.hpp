@@ -74,3 +74,17 @@ void fc_clear_error();
 
 static inline bool fc_is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 static inline int fc_log2i(int x) { int r = 0; while ((1 << r) < x) ++r; return r; }
+
+// Compute units of the current device (cached; 256 if the query fails).
+inline int fc_num_cus() {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n_cu = v;
+    else
+      n_cu = 256;
+  }
+  return n_cu;
+}

@@ -321,20 +321,6 @@ struct Gemm8 {
   }
 };
 
-// Compute units of the current device (cached; 256 if the query fails).
-inline int fc_num_cus() {
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n_cu = v;
-    else
-      n_cu = 256;
-  }
-  return n_cu;
-}
-
 // Tile height of Gemm8 for an M-row product with n_tiles_n 256-wide column tiles:
 // the one with fewer rounds of workgroups over the device's CUs, weighting a
 // 128-row tile (three stages) at 0.62 of a 256-row one (two stages): measured

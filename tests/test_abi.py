@@ -103,7 +103,7 @@ def test_attention_argument_checks():
     base = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, block_table=FAKE, max_pages_per_seq=4,
                 page_size=16, cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, B=2, max_seqlen_q=8, T_k=64,
                 n_heads=2, head_dim=128, softmax_scale=0.088, out=FAKE, importance=FAKE,
-                accumulate=0, workspace=FAKE, workspace_bytes=1 << 20, dtype=fc.FC_DTYPE_BF16)
+                accumulate=0, workspace=FAKE, workspace_bytes=1 << 26, dtype=fc.FC_DTYPE_BF16)
 
     def expect(name, **over):
         a = dict(base)
