@@ -47,7 +47,71 @@ def parse():
                          "that the GPU clocks reach their sustained state")
     ap.add_argument("--cpu-seqs", type=int, default=32,
                     help="sequences of the batch the CPU oracle baseline runs")
+    ap.add_argument("--sweep", choices=("batch", "query"), default=None,
+                    help="instead of the benchmark line: step throughput of the C2 layer "
+                         "over batch sizes 1..64 (query 64 window + 64 tracked) or over query "
+                         "lengths 32..512 per sequence (B=32); one JSON line per point")
     return ap.parse_args()
+
+
+def sweep_main(args):
+    """Throughput of the C2-shaped step against batch size or query length (the
+    pages' throughput-vs-batch-size and query-size measurements, on synthetic
+    inputs of this layer shape)."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd import workload as W
+    from kv_cache_attention_step_amd.runner import StepBuffers
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    if args.sweep == "batch":
+        points = [dict(batch=b) for b in (1, 2, 4, 8, 16, 32, 64)]
+    else:
+        points = [dict(window=q // 2, track=q // 2) for q in (32, 64, 128, 256, 512)]
+    for pt in points:
+        cfg = dataclasses.replace(CF.C2, **pt)
+        inp = W.make_step_inputs(cfg)
+        bufs = StepBuffers(inp, device="cuda:0")
+
+        def one_step(ev=None):
+            with torch.cuda.stream(stream):
+                flush.fill_(1)
+            if ev is not None:
+                ev[0].record(stream)
+            bufs.qkv(stream)
+            if ev is not None:
+                ev[1].record(stream)
+            bufs.attention(stream)
+            if ev is not None:
+                ev[2].record(stream)
+            bufs.topk(stream)
+            if ev is not None:
+                ev[3].record(stream)
+
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            one_step()
+            torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            one_step()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            one_step(evs[i])
+        torch.cuda.synchronize()
+        el = lambda a, b: float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+        ms = el(0, 3)
+        print(json.dumps({"sweep": args.sweep, "batch": inp.B, "query_per_seq": cfg.window + cfg.track,
+                          "query_tokens": inp.T_q, "cache_tokens": inp.T_k,
+                          "ms_per_step": round(ms, 4),
+                          "query_tokens_per_s": round(inp.T_q / (ms * 1e-3), 1),
+                          "qkv_us": round(el(0, 1) * 1e3, 2), "attention_us": round(el(1, 2) * 1e3, 2),
+                          "topk_us": round(el(2, 3) * 1e3, 2)}), flush=True)
+        del bufs
+        torch.cuda.empty_cache()
 
 
 def step_work(inp):
@@ -261,12 +325,14 @@ def stack_main(args):
 
 def main():
     args = parse()
-    if args.config == "C3":
-        return stack_main(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        return sweep_main(args)
+    if args.config == "C3":
+        return stack_main(args)
     import numpy as np
     import torch
     from kv_cache_attention_step_amd import configs as CF

@@ -451,28 +451,31 @@ extern "C" fc_status_t fc_rms_row_scale(const void* x, int32_t M, int32_t N, flo
   return fc_check_launch("fc_rms_row_scale");
 }
 
-// K splits of the bf16 projection with the cache write: 4 when even its
-// 128-row tiles would fill at most a quarter of the CUs (T_q up to
-// qkv_split_rows_max: 128 rows at d = 4096 on 256 CUs); else 1.
-constexpr int QKV_KSPLIT = 4;  // 2: 69 us, 4: 58 us, 8: 69 us at 128 rows x d 4096
-static int qkv_split_rows_max(int d_model) {
-  const int tn = 3 * d_model / QKV_BN;
-  return tn > 0 ? 128 * (fc_num_cus() / (4 * tn)) : 0;
-}
+// K splits of the bf16 projection with the cache write: as many (4, else 2) as
+// the 128-row tiles leave room for on the CUs (one sequence of 128 rows at
+// d = 4096: 48 tiles, 4 splits; two sequences: 96 tiles, 2 splits); else 1.
+// 4 splits beat 2 and 8 at 128 rows (58 vs 69 and 69 us).
 static int qkv_k_splits(int T_q, int d_model, bool write_cache) {
-  return (write_cache && T_q <= qkv_split_rows_max(d_model)) ? QKV_KSPLIT : 1;
+  if (!write_cache) return 1;
+  const long tiles = (long)((T_q + 127) / 128) * (3 * d_model / QKV_BN);
+  const long room = fc_num_cus() / tiles;
+  return room >= 4 ? 4 : room >= 2 ? 2 : 1;
 }
 
 extern "C" size_t fc_qkv_workspace_size(int32_t T_q, int32_t d_model, int32_t head_dim,
                                         int32_t dtype) {
   if (dtype != FC_DTYPE_BF16 || T_q <= 0 || head_dim <= 0 || d_model <= 0) return 0;
   // rotation table, one cache slot per token, then the fp32 partial products
-  // of a K-split projection for up to qkv_split_rows_max rows (so the size
-  // never shrinks as T_q grows: a buffer sized for the largest T_q serves all)
+  // of a K-split projection: S T_q rows of 3 d, where S ceil(T_q / 128) never
+  // exceeds the CUs per 3 d / 256 column tiles. The bound min(4 T_q, 128 CUs /
+  // column tiles) never shrinks as T_q grows, so a buffer sized for the largest
+  // T_q serves all.
   const size_t head = ((size_t)T_q * (head_dim / 2) * sizeof(float2) + (size_t)T_q * sizeof(int32_t) +
                        255) / 256 * 256;
-  const int split_rows = T_q < qkv_split_rows_max(d_model) ? T_q : qkv_split_rows_max(d_model);
-  return head + (size_t)QKV_KSPLIT * split_rows * 3 * d_model * sizeof(float);
+  const long tn = 3L * d_model / QKV_BN;
+  const long cap = tn > 0 ? 128L * (fc_num_cus() / tn) : 0;
+  const long rows = 4L * T_q < cap ? 4L * T_q : cap;
+  return head + (size_t)rows * 3 * d_model * sizeof(float);
 }
 
 extern "C" fc_status_t fc_qkv_rope_cache_write(
