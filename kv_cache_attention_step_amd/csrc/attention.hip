@@ -848,11 +848,11 @@ __global__ __launch_bounds__(64) void attn_f32(const float* __restrict__ q,
 }  // namespace
 
 // Key split (importance path, bf16, at most 128 query rows per sequence): when
-// the (sequence, head) items would occupy at most a quarter of the CUs, each
-// item's keys go to S = min(8, CUs / items) chunks.
+// the (sequence, head) items would occupy at most half of the CUs, each item's
+// keys go to S = min(8, CUs / items) chunks.
 static int attn_key_splits(int B, int n_heads) {
   const int items = B * n_heads, n_cu = fc_num_cus();
-  if (items <= 0 || items * 4 > n_cu) return 1;
+  if (items <= 0 || items * 2 > n_cu) return 1;
   return n_cu / items < 8 ? n_cu / items : 8;
 }
 
