@@ -60,7 +60,7 @@ typedef struct ihipStream_t* fc_stream_t;   /* a hipStream_t */
 typedef enum {
   FC_OK = 0,
   FC_ERR_INVALID_VALUE = 1,   /* null pointer, negative or inconsistent size    */
-  FC_ERR_UNSUPPORTED = 2,     /* valid request that this build does not handle  */
+  FC_ERR_UNSUPPORTED = 2,     /* valid request outside the built shapes/dtypes */
   FC_ERR_WORKSPACE = 3,       /* workspace missing or smaller than required     */
   FC_ERR_HIP = 4              /* a HIP runtime call failed (message has detail) */
 } fc_status_t;
