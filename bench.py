@@ -82,6 +82,7 @@ def sweep_main(args):
                 flush.fill_(1)
             if ev is not None:
                 ev[0].record(stream)
+            bufs.assemble(stream)
             bufs.qkv(stream)
             if ev is not None:
                 ev[1].record(stream)
@@ -146,8 +147,9 @@ def cpu_baseline(inp, n_seqs, budget_s=12.0):
     n = min(n_seqs, inp.B)
     tokens = 0
     t0 = time.perf_counter()
+    positions, _ = O.assemble_batch(inp.tracked, inp.window_start, inp.window_len)
     for b in range(n):
-        s = sequence_inputs(inp, b)
+        s = sequence_inputs(inp, b, positions)
         O.flash_cache_step(s["hidden"], s["positions"], s["cu_q"], s["cu_k"], inp.w_qkv,
                            cfg.n_heads, cfg.head_dim, cfg.rope_base, s["k_cache"], s["v_cache"],
                            s["block_table"], cfg.page_size, s["cand"], cfg.track, cfg.dtype)
@@ -352,6 +354,7 @@ def main():
                 flush.fill_(1)
         if ev is not None:
             ev[0].record(stream)
+        bufs.assemble(stream)
         bufs.qkv(stream)
         if ev is not None:
             ev[1].record(stream)

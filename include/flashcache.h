@@ -34,6 +34,18 @@
  *   - Calls keep no state between them; calls on different streams with
  *     disjoint outputs may run concurrently.
  *   - dtype: FC_DTYPE_BF16 (bf16 storage, fp32 accumulation) or FC_DTYPE_F32.
+ *   - Index inputs (positions, cu_seqlens_*, block_table) are trusted: the
+ *     kernels index memory with them. With the environment variable FC_DEBUG
+ *     set to a non-zero value, fc_qkv_rope_cache_write,
+ *     fc_varlen_bidir_attention, fc_importance_topk, fv_verify_accept and
+ *     fc_assemble_query first wait for the stream, copy these inputs to the
+ *     host and check the preconditions each call can see (offsets start at 0
+ *     and never decrease, totals match; positions >= 0 and distinct per
+ *     sequence when the cache is written; every page a sequence uses has an
+ *     entry >= 0 within max_pages_per_seq; Q_b <= max_seqlen_q), returning
+ *     FC_ERR_INVALID_VALUE with a message before anything is enqueued.
+ *     fc_validate_step_inputs checks all of them, page-id upper bounds
+ *     included, on request.
  *
  * Notation: B sequences; sequence b has query length Q_b (its rows are packed
  * by cu_seqlens_q) and cache length L_b (cu_seqlens_k); H heads of size D;
@@ -114,7 +126,9 @@ const char* fc_version(void);
  *               with few row tiles the fp32 partial products of a K-split
  *               projection; overwritten; NULL allowed when that size is 0;
  *               calls that overlap on one workspace race)
- * Supported: bf16 with D = 128 and d a multiple of 256; f32 with D in {64,128}.
+ * Supported: bf16 with D = 128 and d a multiple of 256 (other head sizes:
+ * FC_ERR_UNSUPPORTED; every bf16 workload here has D = 128, and the bf16
+ * kernels give a wave whole 128-wide heads); f32 with D in {64,128}.
  * page_size must be a power of two in [1, 256]. bf16: hidden, w_qkv, q_out,
  * k_cache, v_cache and workspace must be 16-byte aligned (FC_ERR_INVALID_VALUE
  * otherwise).
@@ -128,8 +142,9 @@ fc_status_t fc_qkv_rope_cache_write(
     fc_stream_t stream);
 
 /* Bytes of device workspace fc_qkv_rope_cache_write needs (0 when none). The
- * K-split decision depends on the current device's compute-unit count, so query
- * it with the device current that the call will run on. */
+ * K-split decision depends on the compute-unit count of the device current at
+ * the time of the query (counted per device), so query it with the device
+ * current that the call will run on. */
 size_t fc_qkv_workspace_size(int32_t T_q, int32_t d_model, int32_t head_dim, int32_t dtype);
 
 /* Bytes of device workspace fc_varlen_bidir_attention needs for these sizes
@@ -252,6 +267,23 @@ fc_status_t fc_linear_residual(const void* x, const void* w, void* h_inout, int3
 fc_status_t fc_assemble_query(const int32_t* topk_pos, const int32_t* topk_count, int32_t k,
                               const int32_t* window_start, const int32_t* cu_seqlens_q,
                               int32_t B, int32_t* positions, fc_stream_t stream);
+
+/*
+ * Debug check of a step's index inputs (the preconditions of
+ * fc_qkv_rope_cache_write and fc_varlen_bidir_attention): cu_seqlens_q and
+ * cu_seqlens_k start at 0, never decrease and end at T_q and T_k; sequence b
+ * uses pages 0 .. ceil(L_b / page_size) - 1 of its block-table row, at most
+ * max_pages_per_seq of them, each entry in [0, num_pages); when positions is
+ * not NULL, the rows of sequence b hold distinct positions in [0, L_b).
+ * Waits for the stream and reads the inputs back to the host; returns FC_OK,
+ * or FC_ERR_INVALID_VALUE with a message naming the first violation. All
+ * pointers are device memory; positions [T_q] may be NULL.
+ */
+fc_status_t fc_validate_step_inputs(const int32_t* positions, const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_k, int32_t B, int32_t T_q,
+                                    int32_t T_k, const int32_t* block_table,
+                                    int32_t max_pages_per_seq, int32_t page_size,
+                                    int32_t num_pages, fc_stream_t stream);
 
 #ifdef __cplusplus
 }

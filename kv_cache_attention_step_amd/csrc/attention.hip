@@ -851,9 +851,10 @@ __global__ __launch_bounds__(64) void attn_f32(const float* __restrict__ q,
 // the (sequence, head) items would occupy at most half of the CUs, each item's
 // keys go to S = min(8, CUs / items) chunks.
 static int attn_key_splits(int B, int n_heads) {
-  const int items = B * n_heads, n_cu = fc_num_cus();
+  const int64_t items = (int64_t)B * n_heads;
+  const int n_cu = fc_num_cus();
   if (items <= 0 || items * 2 > n_cu) return 1;
-  return n_cu / items < 8 ? n_cu / items : 8;
+  return n_cu / items < 8 ? (int)(n_cu / items) : 8;
 }
 
 extern "C" size_t fc_attention_workspace_size(int32_t B, int32_t T_q, int32_t T_k, int32_t n_heads,
@@ -895,6 +896,11 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
              "fc_varlen_bidir_attention: workspace required (fc_attention_workspace_size)");
   if (max_seqlen_q == 0) return FC_OK;
   hipStream_t st = (hipStream_t)stream;
+  if (fc_debug_enabled()) {
+    const fc_status_t s = fc_debug_check_attention(cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q,
+                                                   T_k, block_table, max_pages_per_seq, page_size, st);
+    if (s != FC_OK) return s;
+  }
   const int log2ps = fc_log2i(page_size);
   if (dtype == FC_DTYPE_BF16) {
     FC_REQUIRE(head_dim == AD, FC_ERR_UNSUPPORTED,

@@ -67,6 +67,20 @@ fc_status_t fc_fail(fc_status_t st, const char* fmt, ...);
 fc_status_t fc_check_launch(const char* what);
 void fc_clear_error();
 
+// FC_DEBUG checks (validate.cpp): with the environment variable FC_DEBUG set to
+// a non-zero value, entry points read their index inputs back (waiting for the
+// stream) and reject invalid ones before anything is enqueued.
+bool fc_debug_enabled();
+fc_status_t fc_debug_check_qkv(const int32_t* positions, const int32_t* cu_seqlens_q, int B,
+                               int T_q, const int32_t* block_table, int maxp, int page_size,
+                               bool write_cache, hipStream_t st);
+fc_status_t fc_debug_check_attention(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     int B, int max_seqlen_q, int T_k,
+                                     const int32_t* block_table, int maxp, int page_size,
+                                     hipStream_t st);
+fc_status_t fc_debug_check_offsets(const int32_t* cu, int B, int total, const char* name,
+                                   const char* what, hipStream_t st);
+
 #define FC_REQUIRE(cond, st, ...)                   \
   do {                                              \
     if (!(cond)) return fc_fail((st), __VA_ARGS__); \
@@ -75,16 +89,20 @@ void fc_clear_error();
 static inline bool fc_is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 static inline int fc_log2i(int x) { int r = 0; while ((1 << r) < x) ++r; return r; }
 
-// Compute units of the current device (cached; 256 if the query fails).
+// Compute units of the current device, cached per device id (256 if the query
+// fails). Entries are read and written atomically; concurrent first calls on
+// one device store the same value.
+constexpr int FC_MAX_DEVICES = 64;
 inline int fc_num_cus() {
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n_cu = v;
-    else
-      n_cu = 256;
+  static int n_cu[FC_MAX_DEVICES] = {};
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < FC_MAX_DEVICES) {
+    v = __atomic_load_n(&n_cu[dev], __ATOMIC_RELAXED);
+    if (v > 0) return v;
   }
-  return n_cu;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  if (dev < FC_MAX_DEVICES) __atomic_store_n(&n_cu[dev], v, __ATOMIC_RELAXED);
+  return v;
 }

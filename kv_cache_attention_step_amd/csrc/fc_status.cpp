@@ -1,6 +1,7 @@
 // Status strings, per-thread last-error message and launch checks.
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include "fc_common.hpp"
 
@@ -24,7 +25,11 @@ fc_status_t fc_check_launch(const char* what) {
 }
 
 extern "C" const char* fc_status_string(fc_status_t st) {
-  switch (st) {
+  // a C caller may pass any int; read it as one (an enum load outside the
+  // enumerators' range is undefined in C++)
+  int v;
+  memcpy(&v, &st, sizeof v);
+  switch (v) {
     case FC_OK: return "FC_OK";
     case FC_ERR_INVALID_VALUE: return "FC_ERR_INVALID_VALUE: invalid argument";
     case FC_ERR_UNSUPPORTED: return "FC_ERR_UNSUPPORTED: shape or dtype not supported";

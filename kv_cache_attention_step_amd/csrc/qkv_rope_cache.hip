@@ -509,6 +509,11 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
              "max_pages_per_seq=%d >= 1", page_size, max_pages_per_seq);
   const int log2ps = block_table ? fc_log2i(page_size) : 0;
   hipStream_t st = (hipStream_t)stream;
+  if (fc_debug_enabled()) {
+    const fc_status_t s = fc_debug_check_qkv(positions, cu_seqlens_q, B, T_q, block_table,
+                                             max_pages_per_seq, page_size, write_cache, st);
+    if (s != FC_OK) return s;
+  }
 
   if (dtype == FC_DTYPE_BF16) {
     FC_REQUIRE(head_dim == 128 && d_model % 256 == 0, FC_ERR_UNSUPPORTED,

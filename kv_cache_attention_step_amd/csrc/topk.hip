@@ -233,6 +233,11 @@ extern "C" fc_status_t fc_importance_topk(const float* importance, const int32_t
              "fc_importance_topk: bad sizes B=%d n_heads=%d T_k=%d k=%d", B, n_heads, T_k, k);
   FC_REQUIRE(cu_seqlens_k && topk_pos && topk_count && (importance || T_k == 0),
              FC_ERR_INVALID_VALUE, "fc_importance_topk: NULL required pointer");
+  if (fc_debug_enabled()) {
+    const fc_status_t s = fc_debug_check_offsets(cu_seqlens_k, B, T_k, "cu_seqlens_k",
+                                                 "fc_importance_topk (FC_DEBUG)", (hipStream_t)stream);
+    if (s != FC_OK) return s;
+  }
   hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(TK_THREADS), 0, (hipStream_t)stream, importance,
                      cu_seqlens_k, T_k, n_heads, candidate_mask, k, topk_pos, topk_count,
                      topk_score);
@@ -249,6 +254,11 @@ extern "C" fc_status_t fc_assemble_query(const int32_t* topk_pos, const int32_t*
              "fc_assemble_query: NULL required pointer");
   FC_REQUIRE((topk_count == nullptr) || (topk_pos && k >= 1), FC_ERR_INVALID_VALUE,
              "fc_assemble_query: topk_pos and k >= 1 needed with topk_count");
+  if (fc_debug_enabled()) {
+    const fc_status_t s = fc_debug_check_offsets(cu_seqlens_q, B, -1, "cu_seqlens_q",
+                                                 "fc_assemble_query (FC_DEBUG)", (hipStream_t)stream);
+    if (s != FC_OK) return s;
+  }
   hipLaunchKernelGGL(assemble_kernel, dim3(B), dim3(128), 0, (hipStream_t)stream, topk_pos,
                      topk_count, k, window_start, cu_seqlens_q, positions);
   return fc_check_launch("fc_assemble_query");

@@ -213,6 +213,11 @@ extern "C" fc_status_t fv_verify_accept(const void* logits, int32_t vocab,
              FC_ERR_INVALID_VALUE, "fv_verify_accept: NULL required pointer");
   if (R == 0) return FC_OK;
   hipStream_t st = (hipStream_t)stream;
+  if (fc_debug_enabled()) {
+    const fc_status_t s = fc_debug_check_offsets(cu_positions, B, R / 2, "cu_positions",
+                                                 "fv_verify_accept (FC_DEBUG)", st);
+    if (s != FC_OK) return s;
+  }
   hipLaunchKernelGGL(verify_rows, dim3(R), dim3(VT), 0, st, (const uint16_t*)logits, vocab,
                      cu_positions, B, draft_tokens, tau, argmax, conf, accept_row);
   fc_status_t s = fc_check_launch("fv_verify_accept");

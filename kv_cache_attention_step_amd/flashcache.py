@@ -25,7 +25,8 @@ _STATUS = {0: "FC_OK", 1: "FC_ERR_INVALID_VALUE", 2: "FC_ERR_UNSUPPORTED", 3: "F
 EXPORTS = ("fc_status_string", "fc_last_error", "fc_version", "fc_qkv_rope_cache_write",
            "fc_qkv_workspace_size",
            "fc_attention_workspace_size", "fc_varlen_bidir_attention", "fc_importance_topk",
-           "fv_verify_accept", "fc_linear_residual", "fc_assemble_query", "fc_rms_row_scale")
+           "fv_verify_accept", "fc_linear_residual", "fc_assemble_query", "fc_rms_row_scale",
+           "fc_validate_step_inputs")
 
 
 class FlashCacheError(RuntimeError):
@@ -57,6 +58,7 @@ _SIGS = {
     "fv_verify_accept": ([P, I32, P, I32, I32, P, F32, P, P, P, P, P], I32),
     "fc_linear_residual": ([P, P, P, I32, I32, I32, I32, P], I32),
     "fc_assemble_query": ([P, P, I32, P, P, I32, P, P], I32),
+    "fc_validate_step_inputs": ([P, P, P, I32, I32, I32, P, I32, I32, I32, P], I32),
 }
 
 
@@ -170,3 +172,11 @@ def fc_assemble_query(topk_pos, topk_count, k, window_start, cu_seqlens_q, B, po
     st = load().fc_assemble_query(_p(topk_pos), _p(topk_count), k, _p(window_start),
                                   _p(cu_seqlens_q), B, _p(positions), _stream(stream))
     _check("fc_assemble_query", st)
+
+
+def fc_validate_step_inputs(positions, cu_seqlens_q, cu_seqlens_k, B, T_q, T_k, block_table,
+                            max_pages_per_seq, page_size, num_pages, stream=None):
+    st = load().fc_validate_step_inputs(_p(positions), _p(cu_seqlens_q), _p(cu_seqlens_k), B, T_q,
+                                        T_k, _p(block_table), max_pages_per_seq, page_size,
+                                        num_pages, _stream(stream))
+    _check("fc_validate_step_inputs", st)

@@ -63,8 +63,18 @@ class StepBuffers:
         self.H, self.D, self.d = cfg.n_heads, cfg.head_dim, cfg.d_model
         self.dtype = dtype_code(inp.dtype)
         self.hidden = to_device(inp.hidden, device)
-        self.positions = to_device(inp.positions, device)
         self.cu_q = to_device(inp.cu_seqlens_q, device)
+        # query positions: given (verify-shaped inputs), or assembled on the device
+        # from the tracked positions and the masked window (step S1)
+        self.assembled = inp.positions is None
+        if self.assembled:
+            self.positions = torch.empty(inp.T_q, dtype=torch.int32, device=device)
+            self.tracked = to_device(np.ascontiguousarray(inp.tracked, np.int32), device) \
+                if inp.tracked.size else None
+            self.tracked_count = to_device(inp.tracked_count, device)
+            self.window_start = to_device(inp.window_start, device)
+        else:
+            self.positions = to_device(inp.positions, device)
         self.cu_k = to_device(inp.cu_seqlens_k, device)
         self.w_qkv = to_device(inp.w_qkv, device)
         self.k_cache = to_device(inp.k_cache, device)
@@ -90,7 +100,16 @@ class StepBuffers:
         self.max_seqlen_q = inp.max_seqlen_q
         self.scale = 1.0 / math.sqrt(self.D)
 
-    # the three calls of one Flash-Cache step
+    # the calls of one Flash-Cache step
+    def assemble(self, stream=None):
+        """Query positions = tracked positions + masked window (nothing to do when
+        the inputs carry explicit positions)."""
+        if not self.assembled:
+            return
+        k = self.inp.tracked.shape[1]
+        fc.fc_assemble_query(self.tracked, self.tracked_count if k else None, max(k, 1),
+                             self.window_start, self.cu_q, self.B, self.positions, stream)
+
     def qkv(self, stream=None):
         cfg = self.cfg
         fc.fc_qkv_rope_cache_write(self.hidden, self.positions, self.cu_q, self.B, self.T_q,
@@ -112,12 +131,14 @@ class StepBuffers:
                               self.k, self.topk_pos, self.topk_count, self.topk_score, stream)
 
     def run(self, stream=None):
+        self.assemble(stream)
         self.qkv(stream)
         self.attention(stream)
         self.topk(stream)
 
     def fetch(self) -> Dict[str, np.ndarray]:
-        return dict(q_out=to_host(self.q_out), attn_out=to_host(self.attn_out),
+        return dict(positions=to_host(self.positions),
+                    q_out=to_host(self.q_out), attn_out=to_host(self.attn_out),
                     slot_mapping=to_host(self.slot_mapping), importance=to_host(self.importance),
                     topk_pos=to_host(self.topk_pos), topk_count=to_host(self.topk_count),
                     topk_score=to_host(self.topk_score), k_cache=to_host(self.k_cache),

@@ -14,8 +14,9 @@ Recipe (the pages give no model weights or data, so everything is synthetic):
   * the masked window is the last `window` positions of the generation; the
     candidates for tracking are the generated positions before it; the initial
     tracked set is a seeded sample of `track` candidates.
-  * query rows of a sequence are its positions in ascending order
-    (tracked positions first, then the window).
+  * the query itself (tracked positions plus window, in ascending order) is
+    not formed here: the product assembles it on the device
+    (fc_assemble_query) and the tests take the oracle's assembly.
 All draws use numpy's PCG64 seeded from the config seed (and a stream tag).
 """
 from dataclasses import dataclass
@@ -60,7 +61,7 @@ class StepInputs:
     cfg: StepConfig
     dtype: str
     hidden: np.ndarray          # [T_q, d]   bf16 bits (uint16) or float32
-    positions: np.ndarray       # [T_q]      int32
+    positions: Optional[np.ndarray]  # [T_q] int32; None: assembled from tracked + window
     cu_seqlens_q: np.ndarray    # [B+1]      int32
     cu_seqlens_k: np.ndarray    # [B+1]      int32
     w_qkv: np.ndarray           # [3d, d]
@@ -72,6 +73,11 @@ class StepInputs:
     cache_len: np.ndarray       # [B]
     window_start: np.ndarray    # [B]
     tracked: np.ndarray         # [B, track] int32 ascending
+    window_len: int = 0         # masked-window tokens per sequence
+
+    @property
+    def tracked_count(self) -> np.ndarray:
+        return np.full(self.B, self.tracked.shape[1], dtype=np.int32)
 
     @property
     def B(self) -> int:
@@ -147,14 +153,11 @@ def make_step_inputs(cfg: StepConfig, tail_nan: bool = False) -> StepInputs:
     B = cfg.batch
     window_start = cache_len - cfg.window
     tracked = np.zeros((B, cfg.track), dtype=np.int32)
-    pos_list = []
     for b in range(B):
         cands = np.arange(prompt_len[b], window_start[b])
-        tr = np.sort(rng.choice(cands, size=cfg.track, replace=False)) if cfg.track else cands[:0]
-        tracked[b] = tr
-        pos_list.append(np.concatenate([tr, np.arange(window_start[b], cache_len[b])]))
-    positions = np.concatenate(pos_list).astype(np.int32)
-    q_lens = np.array([len(p) for p in pos_list], dtype=np.int64)
+        tracked[b] = np.sort(rng.choice(cands, size=cfg.track, replace=False)) if cfg.track else cands[:0]
+    # each query holds its tracked positions and its window, disjoint by construction
+    q_lens = np.full(B, cfg.track + cfg.window, dtype=np.int64)
     cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(cache_len)]).astype(np.int32)
     cand = np.zeros(int(cu_k[-1]), dtype=np.uint8)
@@ -165,11 +168,12 @@ def make_step_inputs(cfg: StepConfig, tail_nan: bool = False) -> StepInputs:
     hidden = _normal(rng_for(cfg.seed, 1), (T_q, d), cfg.hidden_std, cfg.dtype)
     w_qkv = _normal(rng_for(cfg.seed, 2), (3 * d, d), cfg.weight_std, cfg.dtype)
     k_cache, v_cache = draw_cache(cfg, num_pages, rng_for(cfg.seed, 3), cache_len, table, tail_nan)
-    return StepInputs(cfg=cfg, dtype=cfg.dtype, hidden=hidden, positions=positions,
+    return StepInputs(cfg=cfg, dtype=cfg.dtype, hidden=hidden, positions=None,
                       cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, w_qkv=w_qkv,
                       k_cache=k_cache, v_cache=v_cache, block_table=table, cand_mask=cand,
                       prompt_len=prompt_len.astype(np.int32), cache_len=cache_len.astype(np.int32),
-                      window_start=window_start.astype(np.int32), tracked=tracked)
+                      window_start=window_start.astype(np.int32), tracked=tracked,
+                      window_len=cfg.window)
 
 
 # ---------------------------------------------------------------------------
@@ -325,15 +329,17 @@ def draw_logits(vi: VerifyInputs, row_block: int = 256) -> np.ndarray:
     return out
 
 
-def sequence_inputs(inp: StepInputs, b: int) -> dict:
+def sequence_inputs(inp: StepInputs, b: int, positions: Optional[np.ndarray] = None) -> dict:
     """Sequence b of a batch on its own: its query rows and only its own cache
-    pages (page ids renumbered 0..n-1, `pages` maps them back)."""
+    pages (page ids renumbered 0..n-1, `pages` maps them back). `positions`: the
+    batch's query positions (default: inp.positions)."""
+    positions = inp.positions if positions is None else positions
     cfg = inp.cfg
     q0, q1 = int(inp.cu_seqlens_q[b]), int(inp.cu_seqlens_q[b + 1])
     L = int(inp.cache_len[b])
     n_pages = (L + cfg.page_size - 1) // cfg.page_size
     pages = inp.block_table[b, :n_pages]
-    return dict(hidden=inp.hidden[q0:q1], positions=inp.positions[q0:q1],
+    return dict(hidden=inp.hidden[q0:q1], positions=positions[q0:q1],
                 cu_q=np.array([0, q1 - q0], np.int32), cu_k=np.array([0, L], np.int32),
                 k_cache=inp.k_cache[pages], v_cache=inp.v_cache[pages],
                 block_table=np.arange(n_pages, dtype=np.int32)[None, :], pages=pages,

@@ -84,6 +84,31 @@ def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# query assembly ([FIG] Fig. 2: the fixed-size query of a step is the tracked
+# positions plus the current masked window)
+# ---------------------------------------------------------------------------
+
+def assemble_query(tracked, window_start: int, window_len: int) -> np.ndarray:
+    """Query positions of one sequence: the union of its tracked positions and
+    the masked window [window_start, window_start + window_len), each position
+    once, in ascending order (int64)."""
+    window = np.arange(window_start, window_start + window_len, dtype=np.int64)
+    return np.union1d(np.asarray(tracked, dtype=np.int64), window)
+
+
+def assemble_batch(tracked_rows, window_start, window_len):
+    """assemble_query per sequence. tracked_rows[b]: that sequence's tracked
+    positions; window_len: one length for all sequences or one per sequence.
+    Returns (positions [T_q] int32, cu_seqlens_q [B+1] int32)."""
+    B = len(tracked_rows)
+    wl = np.broadcast_to(np.asarray(window_len, dtype=np.int64), (B,))
+    parts = [assemble_query(tracked_rows[b], int(window_start[b]), int(wl[b])) for b in range(B)]
+    cu = np.concatenate([[0], np.cumsum([len(p) for p in parts])]).astype(np.int32)
+    pos = np.concatenate(parts).astype(np.int32) if B else np.zeros(0, np.int32)
+    return pos, cu
+
+
+# ---------------------------------------------------------------------------
 # QKV projection, RoPE, paged cache write ([NEWS] paragraph 2)
 # ---------------------------------------------------------------------------
 

@@ -101,3 +101,16 @@ def assert_topk_matches(gpu_pos, gpu_cnt, oracle_score, cand, k, what="topk"):
 def compact_sequence(inp, b):
     from kv_cache_attention_step_amd.workload import sequence_inputs
     return sequence_inputs(inp, b)
+
+
+def oracle_positions(inp):
+    """Query positions of a step's inputs as the oracle assembles them (tracked
+    positions + masked window per sequence), or the explicit positions the inputs
+    carry; checks that the assembled sizes agree with cu_seqlens_q."""
+    if inp.positions is not None:
+        return np.asarray(inp.positions, np.int32)
+    B = inp.B
+    rows = [inp.tracked[b, :int(inp.tracked_count[b])] for b in range(B)]
+    pos, cu = O.assemble_batch(rows, inp.window_start, inp.window_len)
+    assert np.array_equal(cu, inp.cu_seqlens_q), "assembled query sizes != cu_seqlens_q"
+    return pos

@@ -163,3 +163,63 @@ def test_last_error_message_names_the_call():
     st = lib.fc_importance_topk(None, None, 0, 0, 0, None, 0, None, None, None, None)
     assert st == 1
     assert b"fc_importance_topk" in lib.fc_last_error()
+
+
+def _sanitized_build(tmp):
+    """Library sources with AddressSanitizer and UndefinedBehaviorSanitizer on
+    their host code (device code unchanged), linked with the C harness into one
+    executable."""
+    import subprocess
+    from concurrent.futures import ThreadPoolExecutor
+    from kv_cache_attention_step_amd import build_lib as BL
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    clang = os.path.join(rocm, "llvm", "bin", "clang")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+    def compile_one(src):
+        obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+        cmd = [BL.hipcc(), "-x", "hip", f"--offload-arch={BL.ARCH}", "-O2", "-g", "-std=c++17",
+               "-fPIC", "-c", os.path.join(BL.CSRC, src), "-o", obj] + san + BL.DEVICE_FLAGS
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, f"{src}: {r.stderr[-3000:]}"
+        return obj
+
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(compile_one, BL.SOURCES))
+    harness = os.path.join(tmp, "abi_host_checks.o")
+    r = subprocess.run([clang, "-std=c11", "-g", "-O1", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"), "-c",
+                        os.path.join(ROOT, "tests", "abi_host_checks.c"), "-o", harness],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    exe = os.path.join(tmp, "abi_host_checks")
+    r = subprocess.run([clang + "++", "-fsanitize=address,undefined", "-o", exe, harness] + objs +
+                       ["-L" + os.path.join(rocm, "lib"), "-lamdhip64",
+                        "-Wl,-rpath," + os.path.join(rocm, "lib")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    return exe
+
+
+@pytest.mark.slow
+def test_host_code_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """Every entry point's argument checks, size queries at edge values and
+    status strings, run from C against the library's host code built with ASan
+    and UBSan: any out-of-bounds access, use after free, signed overflow or
+    other undefined behaviour on the host side aborts the run."""
+    import shutil
+    import subprocess
+    from kv_cache_attention_step_amd import build_lib as BL
+    try:
+        BL.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    exe = _sanitized_build(str(tmp_path))
+    env = dict(os.environ)
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=0:halt_on_error=1"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    env.pop("FC_DEBUG", None)
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0 and "abi host checks ok" in r.stdout, (r.stdout + r.stderr)[-4000:]
+    shutil.rmtree(str(tmp_path), ignore_errors=True)

@@ -29,12 +29,13 @@ def torch_cuda():
     return torch
 
 
-def run_gpu_step(inp, torch):
+def run_gpu_step(inp, torch, keep=False):
     from kv_cache_attention_step_amd.runner import StepBuffers
     bufs = StepBuffers(inp)
     bufs.run()
     torch.cuda.synchronize()
-    return bufs.fetch()
+    got = bufs.fetch()
+    return (got, bufs) if keep else got
 
 
 def check_cache(got_cache, in_cache, ref_rows, slots, page_size, H, dtype, what):
@@ -53,8 +54,14 @@ def check_cache(got_cache, in_cache, ref_rows, slots, page_size, H, dtype, what)
 
 
 def full_parity(inp, got):
+    """Every output of one step against the oracle, every sequence and head:
+    query positions, slot ids and untouched cache bits exactly; q_out, the
+    written K/V rows and the attention output within the bf16 (fp32) bar;
+    importance within its bar; top-k sets exactly outside the near-tie band."""
     cfg = inp.cfg
-    r = O.flash_cache_step(inp.hidden, inp.positions, inp.cu_seqlens_q, inp.cu_seqlens_k,
+    positions = PU.oracle_positions(inp)
+    assert np.array_equal(got["positions"], positions), "query positions (assembly)"
+    r = O.flash_cache_step(inp.hidden, positions, inp.cu_seqlens_q, inp.cu_seqlens_k,
                            inp.w_qkv, cfg.n_heads, cfg.head_dim, cfg.rope_base, inp.k_cache,
                            inp.v_cache, inp.block_table, cfg.page_size, inp.cand_mask, cfg.track,
                            cfg.dtype)
@@ -67,6 +74,15 @@ def full_parity(inp, got):
                 cfg.n_heads, dt, "v_cache")
     PU.assert_close(PU.as_f64(got["attn_out"], dt), r["out"], dt, "attention out")
     PU.assert_importance_close(got["importance"], r["importance"])
+    for b in range(inp.B):
+        q0, q1 = int(inp.cu_seqlens_q[b]), int(inp.cu_seqlens_q[b + 1])
+        k0, k1 = int(inp.cu_seqlens_k[b]), int(inp.cu_seqlens_k[b + 1])
+        if q1 > q0:
+            PU.assert_close(PU.as_f64(got["attn_out"][q0:q1], dt), r["out"][q0:q1], dt,
+                            f"attention out seq {b}")
+        if k1 > k0 and q1 > q0:
+            PU.assert_importance_close(got["importance"][:, k0:k1], r["importance"][:, k0:k1],
+                                       f"importance seq {b}")
     score = r["importance"].sum(0)
     n_near = 0
     for b in range(inp.B):
@@ -98,7 +114,8 @@ def test_small_bf16_varlen_step_with_nan_tails(torch_cuda):
 
 
 def test_small_page_size_path(torch_cuda):
-    """page_size 4 (< 16 keys of a load group span several pages)."""
+    """page_size 4 (< 16 keys of a load group span several pages) on the key-split
+    path (3 sequences x 4 heads: few (sequence, head) items)."""
     cfg = dataclasses.replace(SMALL_BF16, name="C2-ps4", seed=24, page_size=4)
     _say("case C2-small bf16, page size 4, NaN tails")
     inp = W.make_step_inputs(cfg, tail_nan=True)
@@ -108,12 +125,43 @@ def test_small_page_size_path(torch_cuda):
 
 def test_large_page_size_path(torch_cuda):
     """page_size 64: four 16-key load groups share a page; the last page of a
-    sequence is partly past its end (NaN tails there must never be read)."""
+    sequence is partly past its end (NaN tails there must never be read); the
+    key-split path (few (sequence, head) items)."""
     cfg = dataclasses.replace(SMALL_BF16, name="C2-ps64", seed=26, page_size=64)
     _say("case C2-small bf16, page size 64, NaN tails")
     inp = W.make_step_inputs(cfg, tail_nan=True)
     got = run_gpu_step(inp, torch_cuda)
     full_parity(inp, got)
+
+
+WIDE = dataclasses.replace(CF.C2, name="wide", seed=28, batch=9, d_model=2048, n_heads=16,
+                           prompt=(40, 300), gen_len=160, window=48, track=40)
+
+
+@pytest.mark.parametrize("short_q", [False, True])
+@pytest.mark.parametrize("ps", [4, 64])
+def test_page_sizes_on_the_batched_attention_paths(torch_cuda, ps, short_q):
+    """Page sizes 4 and 64 on the paths a full batch takes: 9 sequences x 16
+    heads = 144 (sequence, head) items, more than half of 256 CUs, so the
+    importance path runs one workgroup per item without a key split; 88 query
+    rows per sequence (128-row tiles) or 48 (at most 64 rows: each tile's keys
+    are split over the waves). The same device queries and cache then go
+    through the one-pass path (no importance). NaN fills the slots past each
+    sequence's end."""
+    torch = torch_cuda
+    w = 24 if short_q else 48
+    cfg = dataclasses.replace(WIDE, name=f"wide-ps{ps}-q{2 * w}", seed=28 + ps + w, page_size=ps,
+                              window=w, track=w if short_q else 40)
+    _say(f"case page size {ps}, {cfg.window + cfg.track} query rows, 144 items")
+    inp = W.make_step_inputs(cfg, tail_nan=True)
+    assert inp.B * cfg.n_heads * 2 > 256 and (inp.max_seqlen_q <= 64) == short_q
+    got, bufs = run_gpu_step(inp, torch, keep=True)
+    r, _ = full_parity(inp, got)
+    bufs.attention(importance=False)
+    torch.cuda.synchronize()
+    from kv_cache_attention_step_amd.runner import to_host
+    PU.assert_close(PU.as_f64(to_host(bufs.attn_out), "bf16"), r["out"], "bf16",
+                    "one-pass attention out")
 
 
 def test_many_sequences(torch_cuda):
@@ -145,74 +193,48 @@ def test_c1_single_layer_step(torch_cuda):
     full_parity(inp, got)
 
 
-def test_c2_full_size_sampled(torch_cuda):
-    """Full C2 shapes in the launch configuration the benchmark times; the oracle
-    recomputes two whole sequences (all heads) and invariants cover the rest."""
-    _say("case C2 full size, sampled sequences")
+def test_c2_full_size_every_sequence(torch_cuda):
+    """The batched step at full size (B=32, d=4096, caches 768..1536, 128 query
+    rows each) in the launch configuration the benchmark times: every output of
+    every sequence against the oracle, plus the column-sum invariant."""
+    _say("case C2 full size, all 32 sequences")
     cfg = CF.C2
     inp = W.make_step_inputs(cfg)
     got = run_gpu_step(inp, torch_cuda)
-    dt = cfg.dtype
-    H, D = cfg.n_heads, cfg.head_dim
-    # invariants over every sequence and head: column sums add up to Q_b per head
     imp = got["importance"].astype(np.float64)
     assert np.all(np.isfinite(imp)) and np.all(imp >= 0)
     for b in range(inp.B):
         k0, k1 = int(inp.cu_seqlens_k[b]), int(inp.cu_seqlens_k[b + 1])
         qb = int(inp.cu_seqlens_q[b + 1] - inp.cu_seqlens_q[b])
         np.testing.assert_allclose(imp[:, k0:k1].sum(1), qb, rtol=2e-4)
-        assert int(got["topk_count"][b]) == cfg.track
-    assert np.all(np.isfinite(PU.as_f64(got["attn_out"], dt)))
-    # two sampled sequences in full
-    for b in (0, inp.B - 1):
-        s = PU.compact_sequence(inp, b)
-        r = O.flash_cache_step(s["hidden"], s["positions"], s["cu_q"], s["cu_k"], inp.w_qkv, H, D,
-                               cfg.rope_base, s["k_cache"], s["v_cache"], s["block_table"],
-                               cfg.page_size, s["cand"], cfg.track, dt)
-        q0, q1 = s["q0"], s["q1"]
-        # slots in the real page numbering
-        slot_real = s["pages"][r["slot_mapping"] // cfg.page_size] * cfg.page_size + \
-            r["slot_mapping"] % cfg.page_size
-        assert np.array_equal(got["slot_mapping"][q0:q1].astype(np.int64), slot_real)
-        PU.assert_close(PU.as_f64(got["q_out"][q0:q1], dt), r["q"], dt, f"q_out seq {b}")
-        pg, off = slot_real // cfg.page_size, slot_real % cfg.page_size
-        PU.assert_close(PU.as_f64(got["k_cache"][pg, :, off, :], dt), r["k"], dt, f"k seq {b}")
-        PU.assert_close(PU.as_f64(got["v_cache"][pg, :, off, :], dt), r["v"], dt, f"v seq {b}")
-        PU.assert_close(PU.as_f64(got["attn_out"][q0:q1], dt), r["out"], dt, f"attn seq {b}")
-        k0, k1 = int(inp.cu_seqlens_k[b]), int(inp.cu_seqlens_k[b + 1])
-        PU.assert_importance_close(got["importance"][:, k0:k1], r["importance"], f"imp seq {b}")
-        PU.assert_topk_matches(got["topk_pos"][b], int(got["topk_count"][b]),
-                               r["importance"].sum(0), s["cand"], cfg.track, f"topk seq {b}")
+    _say("  oracle over the whole batch")
+    full_parity(inp, got)
 
 
 def test_c2_shaped_ragged_row_tiles(torch_cuda):
     """C2-shaped layers with 9 sequences (1152 query tokens): the projection runs
     256-row tiles (fewer rounds of workgroups than 128-row ones) and the last row
-    tile is half empty; sequences at both ends and the one crossing that tile's
-    first row are checked in full against the oracle."""
+    tile is half empty; every sequence against the oracle."""
     _say("case C2-shaped, 9 sequences (ragged 256-row tiles)")
     cfg = dataclasses.replace(CF.C2, name="C2-9", seed=57, batch=9)
     inp = W.make_step_inputs(cfg)
     assert inp.T_q == 1152
     got = run_gpu_step(inp, torch_cuda)
-    dt = cfg.dtype
-    H, D = cfg.n_heads, cfg.head_dim
-    for b in (0, 4, 8):   # sequence 8 holds rows 1024..1151: the partial tile
-        s = PU.compact_sequence(inp, b)
-        r = O.flash_cache_step(s["hidden"], s["positions"], s["cu_q"], s["cu_k"], inp.w_qkv, H, D,
-                               cfg.rope_base, s["k_cache"], s["v_cache"], s["block_table"],
-                               cfg.page_size, s["cand"], cfg.track, dt)
-        q0, q1 = s["q0"], s["q1"]
-        slot_real = s["pages"][r["slot_mapping"] // cfg.page_size] * cfg.page_size + \
-            r["slot_mapping"] % cfg.page_size
-        assert np.array_equal(got["slot_mapping"][q0:q1].astype(np.int64), slot_real)
-        PU.assert_close(PU.as_f64(got["q_out"][q0:q1], dt), r["q"], dt, f"q_out seq {b}")
-        pg, off = slot_real // cfg.page_size, slot_real % cfg.page_size
-        PU.assert_close(PU.as_f64(got["k_cache"][pg, :, off, :], dt), r["k"], dt, f"k seq {b}")
-        PU.assert_close(PU.as_f64(got["v_cache"][pg, :, off, :], dt), r["v"], dt, f"v seq {b}")
-        PU.assert_close(PU.as_f64(got["attn_out"][q0:q1], dt), r["out"], dt, f"attn seq {b}")
-        k0, k1 = int(inp.cu_seqlens_k[b]), int(inp.cu_seqlens_k[b + 1])
-        PU.assert_importance_close(got["importance"][:, k0:k1], r["importance"], f"imp seq {b}")
+    full_parity(inp, got)
+
+
+@pytest.mark.parametrize("B", [2, 4])
+def test_c2_shape_key_split(torch_cuda, B):
+    """The C2 layer shape with few sequences: B=4 (128 (sequence, head) items)
+    splits each item's keys in S=2 chunks and B=2 (64 items) in S=4 on a
+    256-CU device, each chunk several 64-key tiles long; 128 query rows and
+    ragged cache lengths per sequence; every output against the oracle."""
+    _say(f"case C2 shape, B={B} (attention key split)")
+    cfg = dataclasses.replace(CF.C2, name=f"C2-B{B}", seed=60 + B, batch=B)
+    inp = W.make_step_inputs(cfg, tail_nan=True)
+    assert np.any(inp.cache_len % 64 != 0)
+    got = run_gpu_step(inp, torch_cuda)
+    full_parity(inp, got)
 
 
 def test_c2_deterministic(torch_cuda):
@@ -295,13 +317,16 @@ def test_topk_length_capacity(torch_cuda):
     assert gcnt[1] == -1 and np.all(gpos[1] == -1) and np.all(np.isnan(gsc[1])), "over-long sequence"
 
 
-@pytest.mark.parametrize("T", [200, 3000])
-def test_qkv_row_scale_both_tile_heights(torch_cuda, T):
+@pytest.mark.parametrize("T", [200, 1300, 3000])
+def test_qkv_row_scale_every_projection_path(torch_cuda, T):
     """Projection of RMS-normalised inputs (the layer stack's use: a per-row scale
     from fc_rms_row_scale, folded into the rotation table for Q and K and applied
-    to V) at a row count that takes the 128-row tile (T=200) and one that takes
-    the 256-row tile (T=3000); sampled rows against the oracle's normalised
-    projection, cache slots bit-exact, untouched cache rows unchanged."""
+    to V) at d = 1024 (12 column tiles of 256) on each projection path of a
+    256-CU device: T=200 (24 tiles of 128 rows: K split in 4, partial products
+    then the split epilogue), T=1300 (132 tiles of 128 rows: one pass, 128-row
+    tiles), T=3000 (persistent 256-row tiles); sampled rows against the
+    oracle's normalised projection, cache slots bit-exact, untouched cache rows
+    unchanged."""
     torch = torch_cuda
     from kv_cache_attention_step_amd import flashcache as fc
     from kv_cache_attention_step_amd.runner import to_device, to_host

@@ -48,6 +48,44 @@ def test_round_bf16_matches_integer_rounding_of_float32_bits():
 
 
 # ---------------------------------------------------------------------------
+# query assembly (tracked positions + masked window)
+# ---------------------------------------------------------------------------
+
+def test_query_assembly_golden():
+    g = _golden("query_assembly.json")
+    for case in g["cases"]:
+        got = O.assemble_query(case["tracked"], case["window_start"], case["window_len"])
+        np.testing.assert_array_equal(got, case["expected"])
+
+
+def test_query_assembly_properties_and_batch_layout():
+    """Random tracked subsets of the decoded positions before the window: the
+    query holds every tracked and every window position once, ascending, so its
+    size is |tracked| + W; the batch form packs sequences by cu_seqlens_q."""
+    rng = np.random.default_rng(21)
+    tracked_rows, starts, wl = [], [], []
+    for b in range(6):
+        P = int(rng.integers(1, 50))
+        G = int(rng.integers(20, 80))
+        W_ = int(rng.integers(0, 16))
+        cand = np.arange(P, P + G - W_)
+        k = int(rng.integers(0, len(cand) + 1))
+        tr = rng.choice(cand, size=k, replace=False)
+        q = O.assemble_query(tr, P + G - W_, W_)
+        assert len(q) == k + W_
+        assert np.all(np.diff(q) > 0)
+        assert set(q.tolist()) == set(tr.tolist()) | set(range(P + G - W_, P + G))
+        tracked_rows.append(tr)
+        starts.append(P + G - W_)
+        wl.append(W_)
+    pos, cu = O.assemble_batch(tracked_rows, starts, wl)
+    assert cu[0] == 0 and len(cu) == 7 and cu[-1] == len(pos)
+    for b in range(6):
+        np.testing.assert_array_equal(pos[cu[b]:cu[b + 1]],
+                                      O.assemble_query(tracked_rows[b], starts[b], wl[b]))
+
+
+# ---------------------------------------------------------------------------
 # projection
 # ---------------------------------------------------------------------------
 
@@ -349,15 +387,29 @@ def test_topk_golden_ties_and_candidates():
         assert np.all(pos[0, n:] == -1)
 
 
-def test_head_sum_float32_is_sequential_rounding():
-    rng = np.random.default_rng(13)
-    imp = rng.random((32, 50)) * 3
-    s = O.head_sum(imp, as_float32=True)
-    for j in range(50):
-        acc = np.float32(0)
-        for h in range(32):
-            acc = np.float32(acc + np.float32(imp[h, j]))
-        assert s[j] == acc
+def test_head_sum_float32_rounds_every_addition_in_head_order():
+    """Hand-derived fp32 values where per-addition rounding and the head order
+    decide the result (fp32 spacing is 2^-23 on [1, 2) and 2^-22 on [2, 4)):
+      col 0: heads (1, 2^-24, 2^-24): 1 + 2^-24 is a tie between 1 and 1 + 2^-23;
+             ties go to the even significand (1); the second 2^-24 ties again -> 1
+             (the exact sum 1 + 2^-23 is representable).
+      col 1: heads (2^-24, 2^-24, 1): 2^-23 + 1 is exact -> 1 + 2^-23.
+      col 2: heads (2^-24, 1, 2^-24): 2^-24 + 1 ties -> 1, then -> 1.
+      col 3: heads (3, 2^-23, 2^-23): each addition is half a spacing above 3, a tie
+             that goes to 3 (even) -> 3 (exact sum 3 + 2^-22, representable).
+      col 4: heads (1, 3 * 2^-24, 0): 1 + 1.5 spacings, a tie between 1 + 2^-23 (odd)
+             and 1 + 2^-22 (even) -> 1 + 2^-22."""
+    e = 2.0 ** -24
+    imp = np.array([[1.0, e, e, 3.0, 1.0],
+                    [e, e, 1.0, 2 * e, 3 * e],
+                    [e, 1.0, e, 2 * e, 0.0]])
+    got = O.head_sum(imp, as_float32=True)
+    assert got.dtype == np.float32
+    expect = [1.0, 1.0 + 2.0 ** -23, 1.0, 3.0, 1.0 + 2.0 ** -22]
+    assert [float(x) for x in got] == expect
+    # the float64 mode keeps the exact sums
+    np.testing.assert_array_equal(O.head_sum(imp)[:4],
+                                  [1.0 + 2.0 ** -23] * 3 + [3.0 + 2.0 ** -22])
 
 
 # ---------------------------------------------------------------------------
@@ -458,7 +510,11 @@ def test_linear_residual_brute_force():
 def test_tiny_step_chain_properties():
     from kv_cache_attention_step_amd.configs import C0
     inp = W.make_step_inputs(C0)
-    r = O.flash_cache_step(inp.hidden, inp.positions, inp.cu_seqlens_q, inp.cu_seqlens_k,
+    positions, cu_q = O.assemble_batch(inp.tracked, inp.window_start, inp.window_len)
+    np.testing.assert_array_equal(cu_q, inp.cu_seqlens_q)
+    # query = 16 tracked positions from the decoded range, then the window 112..127
+    np.testing.assert_array_equal(positions[16:], np.arange(112, 128))
+    r = O.flash_cache_step(inp.hidden, positions, inp.cu_seqlens_q, inp.cu_seqlens_k,
                            inp.w_qkv, C0.n_heads, C0.head_dim, C0.rope_base, inp.k_cache,
                            inp.v_cache, inp.block_table, C0.page_size, inp.cand_mask, C0.track,
                            C0.dtype)
