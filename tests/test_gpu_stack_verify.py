@@ -105,36 +105,49 @@ def test_layer_stack_chain_small(torch_cuda):
             f"step {st}: tracked sets differ within the near-tie band; chain diverges"
 
 
-def _layer_oracle_check(cfg, l, snap, drv, cand, what):
-    """One layer of the stack, teacher-forced: the oracle runs on exactly the
-    inputs the GPU layer saw (hidden state, query positions, the layer's cache
-    before the write) for every sequence; the output projection is checked on
-    the GPU's own attention output."""
+def _layer_oracle_check(cfg, l, snap, drv, what):
+    """One layer of the stack, teacher-forced on the inputs the GPU layer saw,
+    every sequence. Projection: the oracle's fp64 q, k, v of the layer's hidden
+    state (RMS-normalised) against the GPU's q_out and written cache rows; every
+    other cache slot keeps its bytes. Attention and importance, kernel-isolated:
+    the oracle attends with the GPU's own q_out and cache (the bytes the kernel
+    read). Output projection: h + O Wo^T on the GPU's attention output."""
     H, D = cfg.n_heads, cfg.head_dim
     x = drv.steps[snap["step"]]
+    T_q = len(snap["pos"])
     cu_q = np.arange(cfg.batch + 1, dtype=np.int32) * x["Q"]
     wq, wo = W.layer_weights(cfg, l)
-    r = O.flash_cache_step(snap["h_in"], snap["pos"], cu_q, drv.cu_k_np, wq, H, D, cfg.rope_base,
-                           snap["kc"], snap["vc"], drv.table, cfg.page_size, cand, cfg.track,
-                           "bf16", rms_eps=cfg.rms_eps)
-    PU.assert_close(O.bf16_to_f64(snap["q"]), r["q"], "bf16", f"{what}: q")
-    PU.assert_close(O.bf16_to_f64(snap["o"]), r["out"], "bf16", f"{what}: attention out")
-    PU.assert_importance_close(snap["imp"], r["importance"], f"{what}: importance")
+    proj = O.qkv_rope_cache_write(snap["h_in"], snap["pos"], cu_q, wq, H, D, cfg.rope_base,
+                                  snap["kc"], snap["vc"], drv.table, cfg.page_size, "bf16",
+                                  rms_eps=cfg.rms_eps)
+    PU.assert_close(O.bf16_to_f64(snap["q"]), proj["q"], "bf16", f"{what}: q")
+    slots = proj["slot_mapping"]
+    pg, off = slots // cfg.page_size, slots % cfg.page_size
+    PU.assert_close(O.bf16_to_f64(snap["kc_after"][pg, :, off, :]), proj["k"], "bf16", f"{what}: K rows")
+    PU.assert_close(O.bf16_to_f64(snap["vc_after"][pg, :, off, :]), proj["v"], "bf16", f"{what}: V rows")
+    for name in ("kc", "vc"):
+        before = snap[name].transpose(0, 2, 1, 3).reshape(-1, H, D).copy()
+        after = snap[name + "_after"].transpose(0, 2, 1, 3).reshape(-1, H, D).copy()
+        before[slots] = 0
+        after[slots] = 0
+        assert np.array_equal(before, after), f"{what}: {name} changed outside the written slots"
+    out, imp = O.varlen_attention(O.bf16_to_f64(snap["q"]), O.bf16_to_f64(snap["kc_after"]),
+                                  O.bf16_to_f64(snap["vc_after"]), drv.table, cfg.page_size, cu_q,
+                                  drv.cu_k_np, 1.0 / math.sqrt(D))
+    PU.assert_close(O.bf16_to_f64(snap["o"]), out, "bf16", f"{what}: attention out")
+    PU.assert_importance_close(snap["imp"], imp, f"{what}: importance")
     for b in range(cfg.batch):
         q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
         k0, k1 = int(drv.cu_k_np[b]), int(drv.cu_k_np[b + 1])
-        PU.assert_close(O.bf16_to_f64(snap["o"][q0:q1]), r["out"][q0:q1], "bf16",
+        PU.assert_close(O.bf16_to_f64(snap["o"][q0:q1]), out[q0:q1], "bf16",
                         f"{what}: attention out seq {b}")
-        PU.assert_importance_close(snap["imp"][:, k0:k1], r["importance"][:, k0:k1],
+        PU.assert_importance_close(snap["imp"][:, k0:k1], imp[:, k0:k1],
                                    f"{what}: importance seq {b}")
-    # written K/V rows at their slots
-    slots = r["slot_mapping"]
-    pg, off = slots // cfg.page_size, slots % cfg.page_size
-    PU.assert_close(O.bf16_to_f64(snap["kc_after"][pg, :, off, :]), r["k"], "bf16", f"{what}: K rows")
-    PU.assert_close(O.bf16_to_f64(snap["vc_after"][pg, :, off, :]), r["v"], "bf16", f"{what}: V rows")
-    # h + O Wo^T on the GPU's attention output (one rounding)
-    ref_h = O.linear_residual(snap["o"].reshape(len(snap["pos"]), -1), wo, snap["h_in"], "bf16")
-    PU.assert_close(O.bf16_to_f64(snap["h_out"]), ref_h, "bf16", f"{what}: h + O Wo^T")
+    # the layer's output is the hidden state carried to the next layer: after 31
+    # residual additions |h| exceeds 8, where half a bf16 step (0.031) is above
+    # 2e-2, so the carried state's magnitude-scaled bar applies
+    ref_h = O.linear_residual(snap["o"].reshape(T_q, -1), wo, snap["h_in"], "bf16")
+    PU.assert_close_chained(O.bf16_to_f64(snap["h_out"]), ref_h, f"{what}: h + O Wo^T")
 
 
 def test_layer_stack_full_size(torch_cuda):
@@ -154,7 +167,7 @@ def test_layer_stack_full_size(torch_cuda):
     _say(f"  inputs ready in {time.time() - t0:.1f} s")
     last = cfg.steps - 1
     L_last = cfg.layers - 1
-    snaps = {0: dict(step=0), L_last: dict(step=last), "s0": dict(step=0)}
+    snaps = {0: dict(step=last), L_last: dict(step=last), "s0": dict(step=0)}
     cache_host = lambda l: (to_host(drv.k_cache[l]).copy(), to_host(drv.v_cache[l]).copy())
 
     def on_layer(st, l):
@@ -231,10 +244,9 @@ def test_layer_stack_full_size(torch_cuda):
     for b in range(cfg.batch):
         PU.assert_close(O.bf16_to_f64(sn["o"][b * Q0:(b + 1) * Q0]), r["out"][b * Q0:(b + 1) * Q0],
                         "bf16", f"stack step 0 layer 0 attention, seq {b}")
-    cand_last = W.step_candidates(cfg, last, drv.prompt_len, drv.cu_k_np)
     for l in (0, L_last):
         _say(f"  oracle: step {last}, layer {l}, teacher-forced, all sequences")
-        _layer_oracle_check(cfg, l, snaps[l], drv, cand_last, f"stack step {last} layer {l}")
+        _layer_oracle_check(cfg, l, snaps[l], drv, f"stack step {last} layer {l}")
 
 
 def test_verify_full_vocab(torch_cuda):
