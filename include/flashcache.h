@@ -188,6 +188,27 @@ fc_status_t fc_varlen_bidir_attention(
     void* workspace, size_t workspace_bytes, int32_t dtype, fc_stream_t stream);
 
 /*
+ * fc_varlen_bidir_attention without a workspace argument, for callers that
+ * cannot allocate device memory (code under stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The arguments and results are
+ * those of fc_varlen_bidir_attention; the workspace is instead a static
+ * device array of FC_ATTN_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * device, held until the process ends. The call allocates nothing.
+ * Sizes whose fc_attention_workspace_size exceeds that array are rejected
+ * with FC_ERR_WORKSPACE before anything is enqueued. Every call on one device
+ * shares that device's array: calls that may overlap in time on one device
+ * (different streams, host threads) race and must be serialised by the
+ * caller. The array needs no clearing between calls.
+ */
+#define FC_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)
+fc_status_t fc_varlen_bidir_attention_noalloc(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+    int32_t max_pages_per_seq, int32_t page_size, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, int32_t B, int32_t max_seqlen_q, int32_t T_k, int32_t n_heads,
+    int32_t head_dim, float softmax_scale, void* out, float* importance, int32_t accumulate,
+    int32_t dtype, fc_stream_t stream);
+
+/*
  * Top-k reselection of the tracked positions ([FIG] Fig. 2: tracked positions
  * are the top-k decoded tokens by attention importance).
  *

@@ -870,13 +870,12 @@ extern "C" size_t fc_attention_workspace_size(int32_t B, int32_t T_q, int32_t T_
   return bytes;
 }
 
-extern "C" fc_status_t fc_varlen_bidir_attention(
+static fc_status_t attention_entry(
     const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
     int32_t max_pages_per_seq, int32_t page_size, const int32_t* cu_seqlens_q,
     const int32_t* cu_seqlens_k, int32_t B, int32_t max_seqlen_q, int32_t T_k, int32_t n_heads,
     int32_t head_dim, float softmax_scale, void* out, float* importance, int32_t accumulate,
     void* workspace, size_t workspace_bytes, int32_t dtype, fc_stream_t stream) {
-  fc_clear_error();
   FC_REQUIRE(B >= 1 && n_heads >= 1 && max_seqlen_q >= 0 && T_k >= 0, FC_ERR_INVALID_VALUE,
              "fc_varlen_bidir_attention: bad sizes B=%d n_heads=%d max_seqlen_q=%d T_k=%d", B,
              n_heads, max_seqlen_q, T_k);
@@ -972,4 +971,73 @@ extern "C" fc_status_t fc_varlen_bidir_attention(
                      log2ps, cu_seqlens_q, cu_seqlens_k, n_heads, head_dim, softmax_scale,
                      (float*)out, importance, T_k, accumulate ? 1 : 0);
   return fc_check_launch("fc_varlen_bidir_attention");
+}
+
+extern "C" fc_status_t fc_varlen_bidir_attention(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+    int32_t max_pages_per_seq, int32_t page_size, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, int32_t B, int32_t max_seqlen_q, int32_t T_k, int32_t n_heads,
+    int32_t head_dim, float softmax_scale, void* out, float* importance, int32_t accumulate,
+    void* workspace, size_t workspace_bytes, int32_t dtype, fc_stream_t stream) {
+  fc_clear_error();
+  return attention_entry(q, k_cache, v_cache, block_table, max_pages_per_seq, page_size,
+                         cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, T_k, n_heads, head_dim,
+                         softmax_scale, out, importance, accumulate, workspace, workspace_bytes,
+                         dtype, stream);
+}
+
+// ---- the same call without a caller workspace ---------------------------------
+// For callers that cannot allocate device memory. The workspace (longest-first
+// sequence order, key-split statistics and O partials) lives in this file-scope
+// array instead: one copy per device, held for the life of the process. Host
+// code never names the array directly: its device address is looked up once
+// per device (hipGetSymbolAddress, with that device current) and passed to the
+// kernels like a caller's workspace. The kernels write every workspace byte
+// they later read within one call, so nothing needs clearing between calls.
+constexpr size_t FC_ATTN_SCRATCH_BYTES = FC_ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[FC_ATTN_SCRATCH_BYTES];
+static void* g_scratch_addr[FC_MAX_DEVICES];
+
+static fc_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  FC_REQUIRE(e == hipSuccess, FC_ERR_HIP, "fc_varlen_bidir_attention_noalloc: hipGetDevice: %s",
+             hipGetErrorString(e));
+  FC_REQUIRE(dev >= 0 && dev < FC_MAX_DEVICES, FC_ERR_UNSUPPORTED,
+             "fc_varlen_bidir_attention_noalloc: device %d beyond the %d supported", dev,
+             FC_MAX_DEVICES);
+  void* p = __atomic_load_n(&g_scratch_addr[dev], __ATOMIC_ACQUIRE);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    FC_REQUIRE(e == hipSuccess && p != nullptr, FC_ERR_HIP,
+               "fc_varlen_bidir_attention_noalloc: hipGetSymbolAddress(scratch): %s",
+               hipGetErrorString(e));
+    __atomic_store_n(&g_scratch_addr[dev], p, __ATOMIC_RELEASE);
+  }
+  *out = p;
+  return FC_OK;
+}
+
+extern "C" fc_status_t fc_varlen_bidir_attention_noalloc(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+    int32_t max_pages_per_seq, int32_t page_size, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, int32_t B, int32_t max_seqlen_q, int32_t T_k, int32_t n_heads,
+    int32_t head_dim, float softmax_scale, void* out, float* importance, int32_t accumulate,
+    int32_t dtype, fc_stream_t stream) {
+  fc_clear_error();
+  FC_REQUIRE(B >= 1 && n_heads >= 1, FC_ERR_INVALID_VALUE,
+             "fc_varlen_bidir_attention_noalloc: bad sizes B=%d n_heads=%d", B, n_heads);
+  const size_t need = fc_attention_workspace_size(B, 0, T_k, n_heads, head_dim,
+                                                  importance != nullptr);
+  FC_REQUIRE(need <= FC_ATTN_SCRATCH_BYTES, FC_ERR_WORKSPACE,
+             "fc_varlen_bidir_attention_noalloc: these sizes need %zu bytes of workspace, more "
+             "than the %zu-byte static scratch (use fc_varlen_bidir_attention with a workspace)",
+             need, FC_ATTN_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const fc_status_t s = scratch_address(&ws);
+  if (s != FC_OK) return s;
+  return attention_entry(q, k_cache, v_cache, block_table, max_pages_per_seq, page_size,
+                         cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, T_k, n_heads, head_dim,
+                         softmax_scale, out, importance, accumulate, ws, FC_ATTN_SCRATCH_BYTES,
+                         dtype, stream);
 }

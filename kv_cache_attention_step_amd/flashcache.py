@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libflashcache.so")
 FC_DTYPE_F32 = 0
 FC_DTYPE_BF16 = 1
 FC_TOPK_MAX_LEN = 16384
+FC_ATTN_NOALLOC_SCRATCH_BYTES = 24 << 20
 
 _STATUS = {0: "FC_OK", 1: "FC_ERR_INVALID_VALUE", 2: "FC_ERR_UNSUPPORTED", 3: "FC_ERR_WORKSPACE",
            4: "FC_ERR_HIP"}
@@ -26,7 +27,7 @@ EXPORTS = ("fc_status_string", "fc_last_error", "fc_version", "fc_qkv_rope_cache
            "fc_qkv_workspace_size",
            "fc_attention_workspace_size", "fc_varlen_bidir_attention", "fc_importance_topk",
            "fv_verify_accept", "fc_linear_residual", "fc_assemble_query", "fc_rms_row_scale",
-           "fc_validate_step_inputs")
+           "fc_validate_step_inputs", "fc_varlen_bidir_attention_noalloc")
 
 
 class FlashCacheError(RuntimeError):
@@ -59,6 +60,8 @@ _SIGS = {
     "fc_linear_residual": ([P, P, P, I32, I32, I32, I32, P], I32),
     "fc_assemble_query": ([P, P, I32, P, P, I32, P, P], I32),
     "fc_validate_step_inputs": ([P, P, P, I32, I32, I32, P, I32, I32, I32, P], I32),
+    "fc_varlen_bidir_attention_noalloc": ([P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, F32,
+                                           P, P, I32, I32, P], I32),
 }
 
 
@@ -180,3 +183,14 @@ def fc_validate_step_inputs(positions, cu_seqlens_q, cu_seqlens_k, B, T_q, T_k, 
                                         T_k, _p(block_table), max_pages_per_seq, page_size,
                                         num_pages, _stream(stream))
     _check("fc_validate_step_inputs", st)
+
+
+def fc_varlen_bidir_attention_noalloc(q, k_cache, v_cache, block_table, max_pages_per_seq,
+                                      page_size, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, T_k,
+                                      n_heads, head_dim, softmax_scale, out, importance,
+                                      accumulate, dtype, stream=None):
+    st = load().fc_varlen_bidir_attention_noalloc(
+        _p(q), _p(k_cache), _p(v_cache), _p(block_table), max_pages_per_seq, page_size,
+        _p(cu_seqlens_q), _p(cu_seqlens_k), B, max_seqlen_q, T_k, n_heads, head_dim,
+        softmax_scale, _p(out), _p(importance), int(bool(accumulate)), dtype, _stream(stream))
+    _check("fc_varlen_bidir_attention_noalloc", st)
