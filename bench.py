@@ -33,8 +33,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the Infinity Cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -47,6 +47,10 @@ def parse():
                          "that the GPU clocks reach their sustained state")
     ap.add_argument("--cpu-seqs", type=int, default=32,
                     help="sequences of the batch the CPU oracle baseline runs")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0,
+                    help="seconds of CPU work for each oracle baseline leg (all threads, 1 thread)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured-peak probes (MFMA rate, KV-cache streaming rate)")
     ap.add_argument("--sweep", choices=("batch", "query"), default=None,
                     help="instead of the benchmark line: step throughput of the C2 layer "
                          "over batch sizes 1..64 (query 64 window + 64 tracked) or over query "
@@ -132,22 +136,16 @@ def step_work(inp):
                 attn_flops=attn_flops, topk_bytes=topk_bytes)
 
 
-def cpu_baseline(inp, n_seqs, budget_s=12.0):
-    """The oracle, untuned, on the leading sequences of the same batch: at most
-    n_seqs of them, stopping once budget_s seconds of CPU work are spent."""
-    import numpy as np
+def _oracle_rate(inp, n_seqs, budget_s):
+    """Query tokens per second of the untuned oracle over the leading sequences
+    of the batch (full step each), stopping once budget_s seconds are spent."""
     from kv_cache_attention_step_amd.workload import sequence_inputs
     from oracle import flashcache_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     cfg = inp.cfg
     n = min(n_seqs, inp.B)
     tokens = 0
-    t0 = time.perf_counter()
     positions, _ = O.assemble_batch(inp.tracked, inp.window_start, inp.window_len)
+    t0 = time.perf_counter()
     for b in range(n):
         s = sequence_inputs(inp, b, positions)
         O.flash_cache_step(s["hidden"], s["positions"], s["cu_q"], s["cu_k"], inp.w_qkv,
@@ -158,11 +156,70 @@ def cpu_baseline(inp, n_seqs, budget_s=12.0):
             n = b + 1
             break
     dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "query-tokens/s", "cores": int(threads),
+    return tokens / dt, n, tokens, dt
+
+
+def cpu_baseline(inp, n_seqs, budget_s=10.0):
+    """The oracle, untuned, on the leading sequences of the same batch, twice:
+    with the BLAS thread pool at its default size and with one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    nproc = os.cpu_count() or 1
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
+    rate, n, tokens, dt = _oracle_rate(inp, n_seqs, budget_s)
+    with threadpool_limits(limits=1):
+        rate1, n1, tokens1, dt1 = _oracle_rate(inp, n_seqs, budget_s)
+    return {"value": round(rate, 1), "unit": "query-tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n} of {inp.B} sequences of the same batch ({tokens} query tokens), "
                       f"full step each (fp64 projection, RoPE, cache write, attention, "
-                      f"importance, top-k); {dt:.1f} s"}
+                      f"importance, top-k); {dt:.1f} s",
+            "host_nproc": nproc, "host_affinity_cpus": affinity,
+            "one_thread": {"value": round(rate1, 1), "unit": "query-tokens/s", "cores": 1,
+                           "sample": f"{n1} sequences ({tokens1} query tokens); {dt1:.1f} s"}}
+
+
+def measured_peaks(torch, bufs, flush, stream, reps=20):
+    """Rates measured on this device: the sustained bf16 MFMA rate (register
+    operands only), and the paged KV cache streamed with the attention
+    kernel's access pattern (K and V once; K, then K and V), on the step's own
+    cache with the Infinity Cache flushed before every run."""
+    import numpy as np
+    from kv_cache_attention_step_amd import flashcache as fc
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(max(4 * n_cu, bufs.B * bufs.H), dtype=torch.float32, device="cuda:0")
+
+    def timed(fn, flush_first):
+        ts = []
+        for i in range(reps + 3):
+            if flush_first:
+                with torch.cuda.stream(stream):
+                    flush.fill_(4)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            if i >= 3:
+                ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+
+    blocks, iters = 4 * n_cu, 4096
+    us = timed(lambda: fc.fc_probe_mfma_bf16(blocks, iters, sink, stream), False)
+    mfma_tflops = blocks * 4 * iters * 8 * 32768.0 / (us * 1e-6) / 1e12
+    inp = bufs.inp
+    kv_bytes = 2.0 * inp.T_k * bufs.H * bufs.D * 2
+    stream_us = {}
+    for passes in (1, 2):
+        stream_us[passes] = timed(lambda: fc.fc_probe_kv_stream(
+            bufs.k_cache, bufs.v_cache, bufs.block_table, inp.max_pages, inp.cfg.page_size,
+            bufs.cu_k, bufs.B, bufs.H, bufs.D, passes, sink, stream), flush is not None)
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "mfma_probe_us": round(us, 1),
+            "kv_stream_one_pass_us": round(stream_us[1], 2),
+            "kv_stream_one_pass_gbs": round(kv_bytes / (stream_us[1] * 1e-6) / 1e9, 1),
+            "kv_stream_two_pass_us": round(stream_us[2], 2),
+            "kv_stream_two_pass_gbs": round(1.5 * kv_bytes / (stream_us[2] * 1e-6) / 1e9, 1),
+            "kv_bytes": kv_bytes}
 
 
 def verify_component(torch, args):
@@ -355,15 +412,17 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         bufs.assemble(stream)
-        bufs.qkv(stream)
         if ev is not None:
             ev[1].record(stream)
-        bufs.attention(stream)
+        bufs.qkv(stream)
         if ev is not None:
             ev[2].record(stream)
-        bufs.topk(stream)
+        bufs.attention(stream)
         if ev is not None:
             ev[3].record(stream)
+        bufs.topk(stream)
+        if ev is not None:
+            ev[4].record(stream)
 
     if args.calib:
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")
@@ -383,54 +442,72 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         one_step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    k1 = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    k2 = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    k3 = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
-    ms_per_step = float(step_ms.mean())
+    seg = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in evs]) * 1e3   # us
+    k0, k1, k2, k3 = seg(0, 1), seg(1, 2), seg(2, 3), seg(3, 4)
+    step_ms = seg(0, 4) * 1e-3
+    ms_per_step = float(np.median(step_ms))
     work = step_work(inp)
-    k1_us, k2_us, k3_us = float(k1.mean()) * 1e3, float(k2.mean()) * 1e3, float(k3.mean()) * 1e3
+    peaks = None if args.no_probes else measured_peaks(torch, bufs, flush, stream)
+
+    def entry(times, bound, amount, peak, mpeak=None):
+        avg = float(times.mean())
+        d = {"avg_us": round(avg, 2), "median_us": round(float(np.median(times)), 2),
+             "bound": bound}
+        rate = amount / (avg * 1e-6) / 1e12   # TFLOP/s or TB/s
+        if bound == "mfma":
+            d.update(achieved_tflops=round(rate, 1), frac=round(rate / peak, 4))
+            if mpeak:
+                d["frac_of_measured_mfma"] = round(rate / mpeak, 4)
+        else:
+            d.update(achieved_gbs=round(rate * 1e3, 1), frac=round(rate * 1e3 / peak, 4))
+            if mpeak:
+                d["frac_of_measured_stream"] = round(rate * 1e3 / mpeak, 4)
+        return d
+
+    mp_mfma = peaks["mfma_bf16_tflops"] if peaks else None
+    mp_hbm = peaks["kv_stream_one_pass_gbs"] if peaks else None
     kernels = {
-        "qkv_rope_cache_write": {
-            "avg_us": round(k1_us, 2), "bound": "mfma",
-            "achieved_tflops": round(work["qkv_flops"] / (k1_us * 1e-6) / 1e12, 1),
-            "frac": round(work["qkv_flops"] / (k1_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
-        "varlen_bidir_attention": {
-            "avg_us": round(k2_us, 2), "bound": "hbm",
-            "achieved_gbs": round(work["attn_bytes"] / (k2_us * 1e-6) / 1e9, 1),
-            "frac": round(work["attn_bytes"] / (k2_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
-        "importance_topk": {
-            "avg_us": round(k3_us, 2), "bound": "hbm",
-            "achieved_gbs": round(work["topk_bytes"] / (k3_us * 1e-6) / 1e9, 1),
-            "frac": round(work["topk_bytes"] / (k3_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "assemble_query": {"avg_us": round(float(k0.mean()), 2),
+                           "median_us": round(float(np.median(k0)), 2), "bound": "launch"},
+        "qkv_rope_cache_write": entry(k1, "mfma", work["qkv_flops"], MFMA_BF16_PEAK_TFLOPS, mp_mfma),
+        "varlen_bidir_attention": entry(k2, "hbm", work["attn_bytes"], HBM_PEAK_GBS, mp_hbm),
+        "importance_topk": entry(k3, "hbm", work["topk_bytes"], HBM_PEAK_GBS, mp_hbm),
     }
+    if peaks:
+        # the importance path reads K twice: the two-pass stream of the same
+        # cache is that design's memory floor
+        kernels["varlen_bidir_attention"]["two_pass_floor_us"] = peaks["kv_stream_two_pass_us"]
     # HBM bytes per launch from the committed counter runs (null once the kernel
     # sources differ from those the counters were taken on)
     from kv_cache_attention_step_amd.profiling import load_traffic
     for name, kd in kernels.items():
-        kd["traffic_bytes"] = load_traffic(TRAFFIC_FILE, name)
-    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+        if name != "assemble_query":
+            kd["traffic_bytes"] = load_traffic(TRAFFIC_FILE, name)
+    dominant = max((k for k in kernels if k != "assemble_query"),
+                   key=lambda k: kernels[k]["avg_us"])
     kd = kernels[dominant]
     if kd["bound"] == "mfma":
         roof = {"bound": "mfma", "kernel": dominant, "achieved": kd["achieved_tflops"],
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kd["frac"],
-                "traffic": kd["traffic_bytes"]}
+                "traffic": kd["traffic_bytes"], "measured_peak": mp_mfma,
+                "frac_of_measured_peak": kd.get("frac_of_measured_mfma")}
     else:
         roof = {"bound": "hbm", "kernel": dominant, "achieved": kd["achieved_gbs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["frac"],
-                "traffic": kd["traffic_bytes"]}
+                "traffic": kd["traffic_bytes"], "measured_peak": mp_hbm,
+                "frac_of_measured_peak": kd.get("frac_of_measured_stream")}
     verify = None if args.no_verify else verify_component(torch, args)
     verify_attn = None if args.no_verify else verify_attention_component(torch, args)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seqs)
+        cpu = cpu_baseline(inp, args.cpu_seqs, args.cpu_budget_s)
     L = inp.cache_len
     out = {
         "metric": "Flash-Cache step query-tokens/s at B=32 + % of HBM/MFMA roofline (1 GPU)",
@@ -453,6 +530,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "measured_peaks": peaks,
+        "timing": {"statistic": "median of the timed steps' HIP-event intervals (kernel "
+                                "entries: mean and median)",
+                   "ms_per_step_mean": round(float(step_ms.mean()), 4)},
         "verify_accept_c4": verify,
         "verify_attention_c4": verify_attn,
         "settle": {"seconds": args.settle_s, "steps": settle_steps},

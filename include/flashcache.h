@@ -306,6 +306,29 @@ fc_status_t fc_validate_step_inputs(const int32_t* positions, const int32_t* cu_
                                     int32_t max_pages_per_seq, int32_t page_size,
                                     int32_t num_pages, fc_stream_t stream);
 
+/*
+ * Measurement probes (diagnostics for benchmarks; not part of the step).
+ *
+ * fc_probe_kv_stream: streams the paged bf16 cache of B sequences with the
+ * attention kernel's own access pattern (one workgroup per (sequence, head),
+ * 64-key tiles through registers into LDS, nontemporal loads) and computes
+ * nothing. k_passes = 1 reads K and V once; k_passes = 2 reads K, then K and V
+ * (the two passes of the importance path). The elapsed time is the floor of
+ * that pattern's memory traffic on the device. head_dim must be 128. sink
+ * [B * n_heads] fp32 is a dummy output (left unchanged in practice).
+ *
+ * fc_probe_mfma_bf16: n_blocks workgroups of 4 waves, each wave running
+ * iters x 8 independent v_mfma_f32_32x32x16_bf16 (32768 flops each) on
+ * register operands: the sustained dense bf16 matrix rate, in flops
+ * n_blocks * 4 * iters * 8 * 32768 over the elapsed time. sink [n_blocks].
+ */
+fc_status_t fc_probe_kv_stream(const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, int32_t max_pages_per_seq,
+                               int32_t page_size, const int32_t* cu_seqlens_k, int32_t B,
+                               int32_t n_heads, int32_t head_dim, int32_t k_passes, float* sink,
+                               fc_stream_t stream);
+fc_status_t fc_probe_mfma_bf16(int32_t n_blocks, int32_t iters, float* sink, fc_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

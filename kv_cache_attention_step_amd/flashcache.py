@@ -27,7 +27,8 @@ EXPORTS = ("fc_status_string", "fc_last_error", "fc_version", "fc_qkv_rope_cache
            "fc_qkv_workspace_size",
            "fc_attention_workspace_size", "fc_varlen_bidir_attention", "fc_importance_topk",
            "fv_verify_accept", "fc_linear_residual", "fc_assemble_query", "fc_rms_row_scale",
-           "fc_validate_step_inputs", "fc_varlen_bidir_attention_noalloc")
+           "fc_validate_step_inputs", "fc_varlen_bidir_attention_noalloc",
+           "fc_probe_kv_stream", "fc_probe_mfma_bf16")
 
 
 class FlashCacheError(RuntimeError):
@@ -60,6 +61,8 @@ _SIGS = {
     "fc_linear_residual": ([P, P, P, I32, I32, I32, I32, P], I32),
     "fc_assemble_query": ([P, P, I32, P, P, I32, P, P], I32),
     "fc_validate_step_inputs": ([P, P, P, I32, I32, I32, P, I32, I32, I32, P], I32),
+    "fc_probe_kv_stream": ([P, P, P, I32, I32, P, I32, I32, I32, I32, P, P], I32),
+    "fc_probe_mfma_bf16": ([I32, I32, P, P], I32),
     "fc_varlen_bidir_attention_noalloc": ([P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, F32,
                                            P, P, I32, I32, P], I32),
 }
@@ -194,3 +197,16 @@ def fc_varlen_bidir_attention_noalloc(q, k_cache, v_cache, block_table, max_page
         _p(cu_seqlens_q), _p(cu_seqlens_k), B, max_seqlen_q, T_k, n_heads, head_dim,
         softmax_scale, _p(out), _p(importance), int(bool(accumulate)), dtype, _stream(stream))
     _check("fc_varlen_bidir_attention_noalloc", st)
+
+
+def fc_probe_kv_stream(k_cache, v_cache, block_table, max_pages_per_seq, page_size, cu_seqlens_k,
+                       B, n_heads, head_dim, k_passes, sink, stream=None):
+    st = load().fc_probe_kv_stream(_p(k_cache), _p(v_cache), _p(block_table), max_pages_per_seq,
+                                   page_size, _p(cu_seqlens_k), B, n_heads, head_dim, k_passes,
+                                   _p(sink), _stream(stream))
+    _check("fc_probe_kv_stream", st)
+
+
+def fc_probe_mfma_bf16(n_blocks, iters, sink, stream=None):
+    st = load().fc_probe_mfma_bf16(n_blocks, iters, _p(sink), _stream(stream))
+    _check("fc_probe_mfma_bf16", st)
