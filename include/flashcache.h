@@ -258,6 +258,74 @@ fc_status_t fv_verify_accept(
     uint8_t* accept_pos, fc_stream_t stream);
 
 /*
+ * Confidence-aware acceptance: threshold unmasking without drafts, the
+ * decoding that Flash-Verify is compared with ([README] section 1: the
+ * confidence-aware Flash-Cache configuration; [FIG] Fig. 6: tokens per
+ * iteration against confidence-aware decoding).
+ *
+ * One logit row per masked position; sequence b owns rows cu_positions[b] ..
+ * cu_positions[b+1]-1. For row r:
+ *   argmax[r] = lowest token id among the row's maxima
+ *   conf[r]   = 1 / sum_v exp(logits[r, v] - logits[r, argmax[r]])   (fp32)
+ *   accept[r] = conf[r] >= tau   (fp32, inclusive)
+ * With at_least_one != 0, a sequence none of whose rows passed accepts its
+ * row of largest conf (equal conf: the lower row), so each step unmasks at
+ * least one token per sequence.
+ * logits [R, vocab] bf16, R = cu_positions[B]; argmax [R] int32, conf [R]
+ * fp32, accept [R] uint8.
+ */
+fc_status_t fv_confidence_accept(const void* logits, int32_t vocab, const int32_t* cu_positions,
+                                 int32_t B, int32_t R, float tau, int32_t at_least_one,
+                                 int32_t* argmax, float* conf, uint8_t* accept,
+                                 fc_stream_t stream);
+
+/*
+ * Flash-Verify's two views with view-private K/V ([NEWS] paragraph 3: drafts
+ * and [MASK] tokens are verified through two views of the same positions; the
+ * fugumt abstract page: KV-cache-driven draft-and-verify).
+ *
+ * Sequence b (cache length L_b = cu_seqlens_k[b+1] - cu_seqlens_k[b]) verifies
+ * positions verify_start[b] .. L_b - 1. Each view v (0 = draft, 1 = [MASK])
+ * attends with its own fresh K/V at those positions and the shared cache at
+ * every earlier one. fv_fork_view_pages makes that a paged cache of its own:
+ * virtual sequence 2b + v gets row 2b + v of view_block_table
+ * [2B, max_pages_per_seq], equal to row b of block_table for the pages before
+ * the one holding verify_start[b], then private page ids
+ * view_page_base + (2b + v) * pages_per_view + i (i = 0, 1, ...) up to the last
+ * page of the sequence, then -1. The private pages are pages of k_cache and
+ * v_cache themselves (the caller reserves 2 B pages_per_view of them from
+ * view_page_base on); the shared positions of the first private page are
+ * copied into it. Then:
+ *   - fc_qkv_rope_cache_write over the 2B virtual sequences (rows of sequence
+ *     b: its draft-view rows, then its [MASK]-view rows, at positions
+ *     verify_start[b] + i; block_table = view_block_table) writes each view's
+ *     fresh K/V into its private pages;
+ *   - fc_varlen_bidir_attention (no importance) over the 2B virtual sequences
+ *     (cu_seqlens_k repeating L_b for both views) attends each view to its own
+ *     cache;
+ *   - fv_commit_accepted copies, for every position p of cu_positions with
+ *     accept_pos[p] != 0, the draft view's K and V rows (all heads) into the
+ *     sequence's shared slot; other slots keep their bytes.
+ * Preconditions (checked under FC_DEBUG): 0 <= verify_start[b] <= L_b, the
+ * sequence's pages from the one holding verify_start[b] to its last number at
+ * most pages_per_view, the reserved pages exist. bf16, head_dim 128; k_cache
+ * and v_cache 16-byte aligned. cu_positions [B+1] counts L_b - verify_start[b]
+ * per sequence; n_positions = cu_positions[B].
+ */
+fc_status_t fv_fork_view_pages(void* k_cache, void* v_cache, const int32_t* block_table,
+                               int32_t max_pages_per_seq, int32_t page_size,
+                               const int32_t* cu_seqlens_k, const int32_t* verify_start,
+                               int32_t B, int32_t n_heads, int32_t head_dim,
+                               int32_t view_page_base, int32_t pages_per_view,
+                               int32_t* view_block_table, fc_stream_t stream);
+fc_status_t fv_commit_accepted(void* k_cache, void* v_cache, const int32_t* block_table,
+                               const int32_t* view_block_table, int32_t max_pages_per_seq,
+                               int32_t page_size, const int32_t* cu_positions,
+                               const int32_t* verify_start, int32_t B, int32_t n_positions,
+                               const uint8_t* accept_pos, int32_t n_heads, int32_t head_dim,
+                               fc_stream_t stream);
+
+/*
  * Per-row RMS normalisation factor for a layer's input in the layer stack:
  * scale[m] = 1 / sqrt(mean_n x[m, n]^2 + eps) (fp32 accumulation, no learned
  * weight). Feeds row_scale of fc_qkv_rope_cache_write. Not part of the pages'

@@ -80,6 +80,9 @@ fc_status_t fc_debug_check_attention(const int32_t* cu_seqlens_q, const int32_t*
                                      hipStream_t st);
 fc_status_t fc_debug_check_offsets(const int32_t* cu, int B, int total, const char* name,
                                    const char* what, hipStream_t st);
+fc_status_t fc_debug_check_views(const int32_t* cu_seqlens_k, const int32_t* verify_start,
+                                 int B, const int32_t* block_table, int maxp, int page_size,
+                                 int pages_per_view, hipStream_t st);
 
 #define FC_REQUIRE(cond, st, ...)                   \
   do {                                              \

@@ -137,6 +137,37 @@ fc_status_t fc_debug_check_offsets(const int32_t* cu, int B, int total, const ch
   return check_offsets(c, B, total, name, what);
 }
 
+fc_status_t fc_debug_check_views(const int32_t* cu_seqlens_k, const int32_t* verify_start,
+                                 int B, const int32_t* block_table, int maxp, int page_size,
+                                 int pages_per_view, hipStream_t st) {
+  const char* what = "fv_fork_view_pages (FC_DEBUG)";
+  std::vector<int32_t> ck, vs, bt;
+  fc_status_t s;
+  if ((s = fetch(cu_seqlens_k, (size_t)B + 1, st, ck, what)) != FC_OK) return s;
+  if ((s = check_offsets(ck, B, -1, "cu_seqlens_k", what)) != FC_OK) return s;
+  if ((s = fetch(verify_start, (size_t)B, st, vs, what)) != FC_OK) return s;
+  if ((s = fetch(block_table, (size_t)B * maxp, st, bt, what)) != FC_OK) return s;
+  for (int b = 0; b < B; ++b) {
+    const int L = ck[b + 1] - ck[b];
+    if (vs[b] < 0 || vs[b] > L)
+      return fc_fail(FC_ERR_INVALID_VALUE, "%s: verify_start[%d] = %d outside [0, %d]", what, b,
+                     vs[b], L);
+    const int n_pages = (L + page_size - 1) / page_size, first = vs[b] / page_size;
+    if (n_pages > maxp)
+      return fc_fail(FC_ERR_INVALID_VALUE, "%s: sequence %d needs %d pages > max_pages_per_seq %d",
+                     what, b, n_pages, maxp);
+    if (n_pages - first > pages_per_view)
+      return fc_fail(FC_ERR_INVALID_VALUE,
+                     "%s: sequence %d verifies %d pages, more than pages_per_view %d", what, b,
+                     n_pages - first, pages_per_view);
+    for (int j = 0; j <= first && j < n_pages; ++j)
+      if (bt[(size_t)b * maxp + j] < 0)
+        return fc_fail(FC_ERR_INVALID_VALUE, "%s: block_table[%d][%d] = %d", what, b, j,
+                       bt[(size_t)b * maxp + j]);
+  }
+  return FC_OK;
+}
+
 extern "C" fc_status_t fc_validate_step_inputs(const int32_t* positions,
                                                const int32_t* cu_seqlens_q,
                                                const int32_t* cu_seqlens_k, int32_t B,

@@ -174,15 +174,20 @@ __global__ __launch_bounds__(VT) void verify_rows(const uint16_t* __restrict__ l
 #pragma unroll
     for (int w = 1; w < VT / 64; ++w) idx = min(idx, s_i[w]);
     const float c = 1.f / s;
-    // row -> (sequence, view, position): rows of sequence b are [2 p0, 2 p1), so
-    // r / 2 lies in [p0, p1)
-    const int b = find_seq_v(cu_p, B, r >> 1);
-    const int p0 = cu_p[b], n = cu_p[b + 1] - p0;
-    const int local = r - 2 * p0;
-    const int i = local >= n ? local - n : local;
     argmax[r] = idx;
     conf[r] = c;
-    accept_row[r] = (uint8_t)(idx == draft[p0 + i] && c >= tau);
+    if (draft) {
+      // two views: row -> (sequence, view, position); rows of sequence b are
+      // [2 p0, 2 p1), so r / 2 lies in [p0, p1)
+      const int b = find_seq_v(cu_p, B, r >> 1);
+      const int p0 = cu_p[b], n = cu_p[b + 1] - p0;
+      const int local = r - 2 * p0;
+      const int i = local >= n ? local - n : local;
+      accept_row[r] = (uint8_t)(idx == draft[p0 + i] && c >= tau);
+    } else {
+      // one view, no drafts: row r is position r, accepted on confidence alone
+      accept_row[r] = (uint8_t)(c >= tau);
+    }
   }
 }
 
@@ -197,7 +202,66 @@ __global__ void verify_positions(const uint8_t* __restrict__ accept_row,
   accept_pos[p] = accept_row[2 * p0 + i] & accept_row[2 * p0 + n + i];
 }
 
+// At least one accepted position per sequence: one wave per sequence; when no
+// row of the sequence passed the threshold, the most confident row is accepted
+// (equal confidences: the lower position).
+__global__ __launch_bounds__(64) void accept_at_least_one(const float* __restrict__ conf,
+                                                          const int32_t* __restrict__ cu_p,
+                                                          uint8_t* __restrict__ accept) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int p0 = cu_p[b], p1 = cu_p[b + 1];
+  if (p1 <= p0) return;
+  int any = 0;
+  float best = -1.f;
+  int best_p = 0x7FFFFFFF;
+  for (int p = p0 + lane; p < p1; p += 64) {
+    any |= accept[p];
+    const float c = conf[p];
+    if (c > best) {  // positions rise with p: the first maximum of this lane is kept
+      best = c;
+      best_p = p;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    any |= __shfl_xor(any, off);
+    const float ob = __shfl_xor(best, off);
+    const int op = __shfl_xor(best_p, off);
+    if (ob > best || (ob == best && op < best_p)) {
+      best = ob;
+      best_p = op;
+    }
+  }
+  if (lane == 0 && !any) accept[best_p] = 1;
+}
+
 }  // namespace
+
+extern "C" fc_status_t fv_confidence_accept(const void* logits, int32_t vocab,
+                                            const int32_t* cu_positions, int32_t B, int32_t R,
+                                            float tau, int32_t at_least_one, int32_t* argmax,
+                                            float* conf, uint8_t* accept, fc_stream_t stream) {
+  fc_clear_error();
+  FC_REQUIRE(B >= 1 && vocab >= 1 && R >= 0, FC_ERR_INVALID_VALUE,
+             "fv_confidence_accept: bad sizes B=%d vocab=%d R=%d", B, vocab, R);
+  FC_REQUIRE(tau > 0.f && tau <= 1.f, FC_ERR_INVALID_VALUE,
+             "fv_confidence_accept: tau=%g must be in (0, 1]", (double)tau);
+  FC_REQUIRE(cu_positions && (R == 0 || (logits && argmax && conf && accept)),
+             FC_ERR_INVALID_VALUE, "fv_confidence_accept: NULL required pointer");
+  if (R == 0) return FC_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (fc_debug_enabled()) {
+    const fc_status_t s = fc_debug_check_offsets(cu_positions, B, R, "cu_positions",
+                                                 "fv_confidence_accept (FC_DEBUG)", st);
+    if (s != FC_OK) return s;
+  }
+  hipLaunchKernelGGL(verify_rows, dim3(R), dim3(VT), 0, st, (const uint16_t*)logits, vocab,
+                     cu_positions, B, (const int32_t*)nullptr, tau, argmax, conf, accept);
+  fc_status_t s = fc_check_launch("fv_confidence_accept");
+  if (s != FC_OK || !at_least_one) return s;
+  hipLaunchKernelGGL(accept_at_least_one, dim3(B), dim3(64), 0, st, conf, cu_positions, accept);
+  return fc_check_launch("fv_confidence_accept");
+}
 
 extern "C" fc_status_t fv_verify_accept(const void* logits, int32_t vocab,
                                         const int32_t* cu_positions, int32_t B, int32_t R,

@@ -28,7 +28,8 @@ EXPORTS = ("fc_status_string", "fc_last_error", "fc_version", "fc_qkv_rope_cache
            "fc_attention_workspace_size", "fc_varlen_bidir_attention", "fc_importance_topk",
            "fv_verify_accept", "fc_linear_residual", "fc_assemble_query", "fc_rms_row_scale",
            "fc_validate_step_inputs", "fc_varlen_bidir_attention_noalloc",
-           "fc_probe_kv_stream", "fc_probe_mfma_bf16")
+           "fc_probe_kv_stream", "fc_probe_mfma_bf16", "fv_confidence_accept",
+           "fv_fork_view_pages", "fv_commit_accepted")
 
 
 class FlashCacheError(RuntimeError):
@@ -61,6 +62,9 @@ _SIGS = {
     "fc_linear_residual": ([P, P, P, I32, I32, I32, I32, P], I32),
     "fc_assemble_query": ([P, P, I32, P, P, I32, P, P], I32),
     "fc_validate_step_inputs": ([P, P, P, I32, I32, I32, P, I32, I32, I32, P], I32),
+    "fv_fork_view_pages": ([P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, P, P], I32),
+    "fv_commit_accepted": ([P, P, P, P, I32, I32, P, P, I32, I32, P, I32, I32, P], I32),
+    "fv_confidence_accept": ([P, I32, P, I32, I32, F32, I32, P, P, P, P], I32),
     "fc_probe_kv_stream": ([P, P, P, I32, I32, P, I32, I32, I32, I32, P, P], I32),
     "fc_probe_mfma_bf16": ([I32, I32, P, P], I32),
     "fc_varlen_bidir_attention_noalloc": ([P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, F32,
@@ -210,3 +214,31 @@ def fc_probe_kv_stream(k_cache, v_cache, block_table, max_pages_per_seq, page_si
 def fc_probe_mfma_bf16(n_blocks, iters, sink, stream=None):
     st = load().fc_probe_mfma_bf16(n_blocks, iters, _p(sink), _stream(stream))
     _check("fc_probe_mfma_bf16", st)
+
+
+def fv_confidence_accept(logits, vocab, cu_positions, B, R, tau, at_least_one, argmax, conf,
+                         accept, stream=None):
+    st = load().fv_confidence_accept(_p(logits), vocab, _p(cu_positions), B, R, tau,
+                                     int(bool(at_least_one)), _p(argmax), _p(conf), _p(accept),
+                                     _stream(stream))
+    _check("fv_confidence_accept", st)
+
+
+def fv_fork_view_pages(k_cache, v_cache, block_table, max_pages_per_seq, page_size, cu_seqlens_k,
+                       verify_start, B, n_heads, head_dim, view_page_base, pages_per_view,
+                       view_block_table, stream=None):
+    st = load().fv_fork_view_pages(_p(k_cache), _p(v_cache), _p(block_table), max_pages_per_seq,
+                                   page_size, _p(cu_seqlens_k), _p(verify_start), B, n_heads,
+                                   head_dim, view_page_base, pages_per_view,
+                                   _p(view_block_table), _stream(stream))
+    _check("fv_fork_view_pages", st)
+
+
+def fv_commit_accepted(k_cache, v_cache, block_table, view_block_table, max_pages_per_seq,
+                       page_size, cu_positions, verify_start, B, n_positions, accept_pos, n_heads,
+                       head_dim, stream=None):
+    st = load().fv_commit_accepted(_p(k_cache), _p(v_cache), _p(block_table),
+                                   _p(view_block_table), max_pages_per_seq, page_size,
+                                   _p(cu_positions), _p(verify_start), B, n_positions,
+                                   _p(accept_pos), n_heads, head_dim, _stream(stream))
+    _check("fv_commit_accepted", st)

@@ -297,3 +297,98 @@ class LayerStackDriver:
                 on_layer(st, l)
         fc.fc_importance_topk(self.importance, self.cu_k, self.B, self.T_k, self.H, x["cand"],
                               self.k, self.topk_pos, self.topk_count, self.topk_score, stream)
+
+
+class TwoViewVerifyBuffers:
+    """Flash-Verify's two views with view-private K/V, then the commit.
+
+    Each sequence b verifies its last n_b positions (verify_start[b] = L_b - n_b)
+    through a draft view and a [MASK] view (rows: n_b draft rows, then n_b mask
+    rows). The cache arrays get pages_per_view spare pages per (sequence, view)
+    after the shared pages; fv_fork_view_pages gives each view a page-table row
+    of its own over them; the fused projection writes each view's fresh K/V
+    there (2B virtual sequences); the one-pass attention attends each view to
+    its own cache; fv_verify_accept decides; fv_commit_accepted copies the
+    accepted positions' draft-view K/V into the shared cache.
+    """
+
+    def __init__(self, vi: VerifyInputs, device="cuda"):
+        torch = _torch()
+        inp = vi.step
+        cfg = vi.cfg
+        self.vi, self.inp, self.cfg, self.device = vi, inp, cfg, device
+        B, H, D, ps = cfg.batch, cfg.n_heads, cfg.head_dim, cfg.page_size
+        self.B, self.H, self.D, self.d, self.ps = B, H, D, cfg.d_model, ps
+        self.dtype = dtype_code(inp.dtype)
+        n = vi.verify_len.astype(np.int64)
+        L = inp.cache_len.astype(np.int64)
+        self.n_pos = int(n.sum())
+        self.pages_per_view = int((int(n.max()) + ps - 1) // ps + 1)
+        num_pages = inp.k_cache.shape[0]
+        self.view_page_base = num_pages
+        total = num_pages + 2 * B * self.pages_per_view
+        et = elem_dtype(inp.dtype)
+        self.k_cache = torch.zeros((total, H, ps, D), dtype=et, device=device)
+        self.v_cache = torch.zeros((total, H, ps, D), dtype=et, device=device)
+        self.k_cache[:num_pages].copy_(to_device(inp.k_cache, device))
+        self.v_cache[:num_pages].copy_(to_device(inp.v_cache, device))
+        self.max_pages = inp.max_pages
+        self.block_table = to_device(inp.block_table, device)
+        self.view_table = torch.full((2 * B, self.max_pages), -1, dtype=torch.int32, device=device)
+        self.verify_start_np = (L - n).astype(np.int32)
+        self.verify_start = to_device(self.verify_start_np, device)
+        self.cu_k = to_device(inp.cu_seqlens_k, device)
+        self.cu_p = to_device(vi.cu_positions, device)
+        # the 2B virtual sequences: (b, draft), (b, mask), ...
+        nv = np.repeat(n, 2)
+        self.cu_q_np = np.concatenate([[0], np.cumsum(nv)]).astype(np.int32)
+        self.cu_kv_np = np.concatenate([[0], np.cumsum(np.repeat(L, 2))]).astype(np.int32)
+        self.cu_q = to_device(self.cu_q_np, device)
+        self.cu_kv = to_device(self.cu_kv_np, device)
+        self.T_q = int(self.cu_q_np[-1])
+        self.T_kv = int(self.cu_kv_np[-1])
+        self.max_q = int(n.max())
+        self.hidden = to_device(inp.hidden, device)
+        self.positions = to_device(inp.positions, device)
+        self.w_qkv = to_device(inp.w_qkv, device)
+        self.q_out = torch.empty((self.T_q, H, D), dtype=et, device=device)
+        self.attn_out = torch.empty((self.T_q, H, D), dtype=et, device=device)
+        self.slot_mapping = torch.empty(self.T_q, dtype=torch.int32, device=device)
+        qws = fc.fc_qkv_workspace_size(self.T_q, self.d, D, self.dtype)
+        self.qkv_ws_bytes = qws
+        self.qkv_workspace = torch.empty(max(qws, 1), dtype=torch.uint8, device=device)
+        ws = fc.fc_attention_workspace_size(2 * B, self.T_q, self.T_kv, H, D, 0)
+        self.ws_bytes = ws
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        self.accept_pos = torch.zeros(self.n_pos, dtype=torch.uint8, device=device)
+        self.scale = 1.0 / math.sqrt(D)
+
+    def fork(self, stream=None):
+        fc.fv_fork_view_pages(self.k_cache, self.v_cache, self.block_table, self.max_pages, self.ps,
+                              self.cu_k, self.verify_start, self.B, self.H, self.D,
+                              self.view_page_base, self.pages_per_view, self.view_table, stream)
+
+    def qkv(self, stream=None):
+        fc.fc_qkv_rope_cache_write(self.hidden, self.positions, self.cu_q, 2 * self.B, self.T_q,
+                                   self.w_qkv, self.d, self.H, self.D, self.cfg.rope_base,
+                                   self.k_cache, self.v_cache, self.view_table, self.max_pages,
+                                   self.ps, self.q_out, self.slot_mapping, self.qkv_workspace,
+                                   self.qkv_ws_bytes, self.dtype, stream)
+
+    def attention(self, stream=None):
+        fc.fc_varlen_bidir_attention(self.q_out, self.k_cache, self.v_cache, self.view_table,
+                                     self.max_pages, self.ps, self.cu_q, self.cu_kv, 2 * self.B,
+                                     self.max_q, self.T_kv, self.H, self.D, self.scale,
+                                     self.attn_out, None, 0, self.workspace, self.ws_bytes,
+                                     self.dtype, stream)
+
+    def commit(self, accept_pos=None, stream=None):
+        fc.fv_commit_accepted(self.k_cache, self.v_cache, self.block_table, self.view_table,
+                              self.max_pages, self.ps, self.cu_p, self.verify_start, self.B,
+                              self.n_pos, self.accept_pos if accept_pos is None else accept_pos,
+                              self.H, self.D, stream)
+
+    def run_views(self, stream=None):
+        self.fork(stream)
+        self.qkv(stream)
+        self.attention(stream)

@@ -36,6 +36,8 @@ Where the pages are silent the oracle takes these readings:
   * verify: argmax with the lowest token id on ties; confidence = the largest
     softmax probability; accept a row when argmax == draft and conf >= tau (both
     as float32); a position is accepted when both of its view rows are.
+  * confidence-aware acceptance: a position is accepted when its confidence
+    alone reaches tau; optionally at least the most confident one per sequence.
 """
 import math
 from itertools import combinations
@@ -341,6 +343,103 @@ def verify_accept(logits_bits, cu_positions, draft, tau):
                 acc[r] = int(a == int(draft[p0 + i]) and np.float32(c) >= tau32)
             acc_pos[p0 + i] = acc[2 * p0 + i] & acc[2 * p0 + n + i]
     return am, conf, acc, acc_pos
+
+
+def two_view_attention(hidden, w_qkv, n_heads, head_dim, rope_base, k_cache, v_cache,
+                       block_table, page_size, cu_positions, verify_start, cache_len, dtype):
+    """Flash-Verify's two views with view-private K/V ([NEWS] paragraph 3: drafts
+    and [MASK] tokens verified through two views of the same positions).
+
+    Sequence b verifies positions verify_start[b] .. cache_len[b]-1 (n_b of
+    them); its hidden rows are n_b draft-view rows then n_b mask-view rows
+    (packed by 2 * cu_positions). Each view projects its own rows at those
+    positions; its keys and values are the shared cache at the earlier
+    positions and its own fresh K/V (rounded to the interface dtype) at the
+    verified ones; its rows attend to all L_b keys of that (reading: each view
+    sees only its own refreshed entries, as a single Flash-Cache step would).
+
+    Returns dict(out [R, H, D], q [R, H, D] unrounded, k, v [R, H, D] fresh,
+    unrounded); rows in the input order.
+    """
+    x = as_f64(hidden, dtype)
+    w = as_f64(w_qkv, dtype)
+    kc = as_f64(k_cache, dtype)
+    vc = as_f64(v_cache, dtype)
+    H, D = n_heads, head_dim
+    d = H * D
+    R = x.shape[0]
+    scale = 1.0 / math.sqrt(D)
+    out = np.zeros((R, H, D))
+    qa = np.zeros((R, H, D))
+    ka = np.zeros((R, H, D))
+    va = np.zeros((R, H, D))
+    for b in range(len(cu_positions) - 1):
+        n = int(cu_positions[b + 1] - cu_positions[b])
+        L, vs = int(cache_len[b]), int(verify_start[b])
+        assert n == L - vs
+        pos = np.arange(vs, L)
+        K = gather_kv(kc, block_table, b, L, page_size)
+        V = gather_kv(vc, block_table, b, L, page_size)
+        for view in (0, 1):
+            r0 = 2 * int(cu_positions[b]) + view * n
+            y = x[r0:r0 + n] @ w.T
+            q = np.stack([rope(y[:, h * D:(h + 1) * D], pos, rope_base) for h in range(H)], axis=1)
+            k = np.stack([rope(y[:, d + h * D:d + (h + 1) * D], pos, rope_base) for h in range(H)],
+                         axis=1)
+            v = y[:, 2 * d:].reshape(n, H, D)
+            Kv, Vv = K.copy(), V.copy()
+            Kv[vs:] = round_to(k, dtype)
+            Vv[vs:] = round_to(v, dtype)
+            qr = round_to(q, dtype)
+            for h in range(H):
+                o, _, _, _ = attention_head(qr[:, h, :], Kv[:, h, :], Vv[:, h, :], scale)
+                out[r0:r0 + n, h] = o
+            qa[r0:r0 + n], ka[r0:r0 + n], va[r0:r0 + n] = q, k, v
+    return dict(out=out, q=qa, k=ka, v=va)
+
+
+def commit_accepted(k_cache, v_cache, block_table, page_size, cu_positions, verify_start,
+                    accept_pos, k_draft, v_draft, dtype):
+    """The shared cache after Flash-Verify's commit: every accepted verified
+    position takes the draft view's fresh K/V (rounded to the interface dtype);
+    every other slot keeps its value. k_draft, v_draft [n_positions, H, D]
+    (position order). Returns float64 copies of the caches."""
+    kc = as_f64(k_cache, dtype).copy()
+    vc = as_f64(v_cache, dtype).copy()
+    for b in range(len(cu_positions) - 1):
+        for i in range(int(cu_positions[b + 1] - cu_positions[b])):
+            p = int(cu_positions[b]) + i
+            if accept_pos[p]:
+                slot = slot_of(block_table, b, int(verify_start[b]) + i, page_size)
+                page, off = divmod(slot, page_size)
+                kc[page, :, off, :] = round_to(k_draft[p], dtype)
+                vc[page, :, off, :] = round_to(v_draft[p], dtype)
+    return kc, vc
+
+
+def confidence_accept(logits_bits, cu_positions, tau, at_least_one):
+    """Confidence-aware acceptance (threshold unmasking, no drafts): one logit
+    row per position. Returns argmax [R] (lowest token id on ties), conf [R]
+    (float64, the largest softmax probability), accept [R]: conf >= tau, both
+    compared as float32. With at_least_one, a sequence with no accepted
+    position accepts its most confident one (equal confidences -> the lower
+    position), so every step unmasks at least one token per sequence (a
+    reading: the pages give no rule for a step where nothing passes)."""
+    R = logits_bits.shape[0]
+    am = np.zeros(R, dtype=np.int64)
+    conf = np.zeros(R, dtype=np.float64)
+    acc = np.zeros(R, dtype=np.uint8)
+    tau32 = np.float32(tau)
+    for r in range(R):
+        a, c = argmax_conf(bf16_to_f64(logits_bits[r]))
+        am[r], conf[r] = a, c
+        acc[r] = int(np.float32(c) >= tau32)
+    if at_least_one:
+        for b in range(len(cu_positions) - 1):
+            p0, p1 = int(cu_positions[b]), int(cu_positions[b + 1])
+            if p1 > p0 and not acc[p0:p1].any():
+                acc[p0 + int(np.argmax(conf[p0:p1]))] = 1   # first maximum
+    return am, conf, acc
 
 
 # ---------------------------------------------------------------------------

@@ -530,3 +530,139 @@ def test_tiny_step_chain_properties():
     cand = np.arange(64, 112)
     best = cand[np.argsort(-score[cand], kind="stable")[:16]]
     np.testing.assert_array_equal(pos, np.sort(best))
+
+
+def test_confidence_accept_golden():
+    """Threshold unmasking on rows whose confidence has a closed form
+    (one logit a among zeros: conf = e^a / (e^a + V - 1))."""
+    g = _golden("confidence_accept.json")
+    bits = W.to_bf16_bits(np.array(g["rows"], np.float32))
+    assert np.array_equal(W.bf16_bits_to_f32(bits), np.array(g["rows"], np.float32))
+    for at_least_one, key in ((False, "expected_accept_threshold_only"),
+                              (True, "expected_accept_at_least_one")):
+        am, conf, acc = O.confidence_accept(bits, g["cu_positions"], g["tau"], at_least_one)
+        np.testing.assert_array_equal(am, g["expected_argmax"])
+        np.testing.assert_allclose(conf, g["expected_conf"], rtol=1e-12)
+        np.testing.assert_array_equal(acc, g[key])
+
+
+def test_confidence_accept_matches_verify_rows_without_drafts():
+    """On random rows the per-row decisions are those of the verify test's
+    rows with the draft comparison dropped: argmax and conf from the same
+    closed forms, accepted iff conf >= tau."""
+    rng = np.random.default_rng(33)
+    V = 50
+    x = rng.normal(0, 2, (12, V))
+    x[3, 7] = 12.0          # a confident row
+    bits = W.to_bf16_bits(x.astype(np.float32))
+    xf = O.bf16_to_f64(bits)
+    am, conf, acc = O.confidence_accept(bits, [0, 5, 12], 0.9, False)
+    for r in range(12):
+        assert am[r] == int(np.flatnonzero(xf[r] == xf[r].max())[0])
+        e = np.exp(xf[r] - xf[r].max())
+        assert abs(conf[r] - 1.0 / e.sum()) < 1e-15
+        assert acc[r] == int(np.float32(conf[r]) >= np.float32(0.9))
+    assert acc[3] == 1 and acc.sum() == 1
+
+
+# ---------------------------------------------------------------------------
+# Flash-Verify's two views with view-private K/V, and the commit
+# ---------------------------------------------------------------------------
+
+def _two_view_case(seed, dtype="f32"):
+    rng = np.random.default_rng(seed)
+    H, D, ps = 2, 8, 4
+    d = H * D
+    L = np.array([13, 9, 16])
+    n = np.array([5, 9, 3])                 # verified positions per sequence
+    vs = L - n
+    B = len(L)
+    n_pages = (L + ps - 1) // ps
+    perm = rng.permutation(int(n_pages.sum()) + 3)
+    table = np.full((B, int(n_pages.max())), -1, np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :n_pages[b]] = perm[o:o + n_pages[b]]
+        o += n_pages[b]
+    num_pages = int(perm.max()) + 1
+    kc = rng.standard_normal((num_pages, H, ps, D)).astype(np.float32)
+    vc = rng.standard_normal((num_pages, H, ps, D)).astype(np.float32)
+    cu_p = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    hidden = rng.standard_normal((2 * int(n.sum()), d)).astype(np.float32)
+    w = (rng.standard_normal((3 * d, d)) * 0.3).astype(np.float32)
+    return dict(H=H, D=D, ps=ps, L=L, n=n, vs=vs, B=B, table=table, kc=kc, vc=vc, cu_p=cu_p,
+                hidden=hidden, w=w, d=d)
+
+
+def test_two_view_attention_is_one_flash_cache_step_per_view():
+    """Each view's output equals an ordinary Flash-Cache step (projection, cache
+    write at the view's positions, attention to the whole cache) run for that
+    view alone on its own copy of the cache: the page-table write and gather
+    path of the step, against the direct substitution of the two-view oracle."""
+    c = _two_view_case(41)
+    r = O.two_view_attention(c["hidden"], c["w"], c["H"], c["D"], 1e4, c["kc"], c["vc"],
+                             c["table"], c["ps"], c["cu_p"], c["vs"], c["L"], "f32")
+    for b in range(c["B"]):
+        n = int(c["n"][b])
+        for view in (0, 1):
+            r0 = 2 * int(c["cu_p"][b]) + view * n
+            pos = np.arange(c["vs"][b], c["L"][b]).astype(np.int32)
+            step = O.flash_cache_step(c["hidden"][r0:r0 + n], pos, np.array([0, n]),
+                                      np.array([0, c["L"][b]]), c["w"], c["H"], c["D"], 1e4,
+                                      c["kc"], c["vc"], c["table"][b:b + 1], c["ps"], None, 1,
+                                      "f32")
+            np.testing.assert_allclose(r["out"][r0:r0 + n], step["out"], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(r["k"][r0:r0 + n], step["k"], rtol=1e-12, atol=1e-12)
+
+
+def test_two_view_attention_identical_views_and_isolation():
+    """Identical hidden rows in both views give identical outputs; changing
+    only the [MASK] view's rows leaves the draft view's output unchanged (the
+    views do not see each other's K/V)."""
+    c = _two_view_case(42)
+    h = c["hidden"].copy()
+    for b in range(c["B"]):
+        n = int(c["n"][b])
+        r0 = 2 * int(c["cu_p"][b])
+        h[r0 + n:r0 + 2 * n] = h[r0:r0 + n]
+    r = O.two_view_attention(h, c["w"], c["H"], c["D"], 1e4, c["kc"], c["vc"], c["table"],
+                             c["ps"], c["cu_p"], c["vs"], c["L"], "f32")
+    h2 = h.copy()
+    for b in range(c["B"]):
+        n = int(c["n"][b])
+        r0 = 2 * int(c["cu_p"][b])
+        np.testing.assert_array_equal(r["out"][r0:r0 + n], r["out"][r0 + n:r0 + 2 * n])
+        h2[r0 + n:r0 + 2 * n] += 1.0
+    r2 = O.two_view_attention(h2, c["w"], c["H"], c["D"], 1e4, c["kc"], c["vc"], c["table"],
+                              c["ps"], c["cu_p"], c["vs"], c["L"], "f32")
+    for b in range(c["B"]):
+        n = int(c["n"][b])
+        r0 = 2 * int(c["cu_p"][b])
+        np.testing.assert_array_equal(r2["out"][r0:r0 + n], r["out"][r0:r0 + n])
+        assert not np.allclose(r2["out"][r0 + n:r0 + 2 * n], r["out"][r0 + n:r0 + 2 * n])
+
+
+def test_commit_writes_accepted_draft_rows_only():
+    c = _two_view_case(43)
+    rng = np.random.default_rng(44)
+    npos = int(c["cu_p"][-1])
+    acc = (rng.random(npos) < 0.5).astype(np.uint8)
+    kd = rng.standard_normal((npos, c["H"], c["D"]))
+    vd = rng.standard_normal((npos, c["H"], c["D"]))
+    kc2, vc2 = O.commit_accepted(c["kc"], c["vc"], c["table"], c["ps"], c["cu_p"], c["vs"], acc,
+                                 kd, vd, "f32")
+    for b in range(c["B"]):
+        K = O.gather_kv(kc2, c["table"], b, int(c["L"][b]), c["ps"])
+        K0 = O.gather_kv(c["kc"].astype(np.float64), c["table"], b, int(c["L"][b]), c["ps"])
+        for j in range(int(c["L"][b])):
+            i = j - int(c["vs"][b])
+            p = int(c["cu_p"][b]) + i
+            if i >= 0 and acc[p]:
+                np.testing.assert_array_equal(K[j], kd[p].astype(np.float32).astype(np.float64))
+            else:
+                np.testing.assert_array_equal(K[j], K0[j])
+    # slots outside every sequence's table are untouched
+    used = {int(x) for x in c["table"].ravel() if x >= 0}
+    for pg in range(c["kc"].shape[0]):
+        if pg not in used:
+            np.testing.assert_array_equal(kc2[pg], c["kc"][pg].astype(np.float64))
