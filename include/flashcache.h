@@ -258,6 +258,29 @@ fc_status_t fv_verify_accept(
     uint8_t* accept_pos, fc_stream_t stream);
 
 /*
+ * The LM head with the Flash-Verify accept test fused in ([NEWS] paragraph 3:
+ * predictions of the two views meeting the confidence threshold are
+ * accepted; the predictions come from the model's logits over the
+ * vocabulary). For every row r of hidden:
+ *   logit[r, v] = hidden[r] . w_lm[v]              (fp32 accumulation, never stored)
+ *   argmax[r]   = lowest v among the row's maxima
+ *   conf[r]     = 1 / sum_v exp(logit[r, v] - logit[r, argmax[r]])
+ * then accept_row / accept_pos exactly as fv_verify_accept (rows of sequence
+ * b: its draft-view rows, then its mask-view rows).
+ * hidden [R, d_model] bf16, w_lm [vocab, d_model] bf16 (16-byte aligned);
+ * workspace of at least fv_lmhead_workspace_size(R, vocab) bytes (per-row
+ * partial maxima and sums; overwritten). Supported: vocab % 256 == 0,
+ * d_model % 64 == 0, vocab * d_model < 2^30.
+ */
+size_t fv_lmhead_workspace_size(int32_t R, int32_t vocab);
+fc_status_t fv_lmhead_verify_accept(const void* hidden, const void* w_lm, int32_t d_model,
+                                    int32_t vocab, const int32_t* cu_positions, int32_t B,
+                                    int32_t R, const int32_t* draft_tokens, float tau,
+                                    void* workspace, size_t workspace_bytes, int32_t* argmax,
+                                    float* conf, uint8_t* accept_row, uint8_t* accept_pos,
+                                    fc_stream_t stream);
+
+/*
  * Confidence-aware acceptance: threshold unmasking without drafts, the
  * decoding that Flash-Verify is compared with ([README] section 1: the
  * confidence-aware Flash-Cache configuration; [FIG] Fig. 6: tokens per

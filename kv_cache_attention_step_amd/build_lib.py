@@ -17,7 +17,7 @@ ARCH = os.environ.get("FC_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["fc_status.cpp", "validate.cpp", "qkv_rope_cache.hip", "attention.hip", "topk.hip",
            "verify.hip", "linear.hip", "probes.hip",
-           "views.hip"]
+           "views.hip", "lmhead.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

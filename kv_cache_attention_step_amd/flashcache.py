@@ -29,7 +29,8 @@ EXPORTS = ("fc_status_string", "fc_last_error", "fc_version", "fc_qkv_rope_cache
            "fv_verify_accept", "fc_linear_residual", "fc_assemble_query", "fc_rms_row_scale",
            "fc_validate_step_inputs", "fc_varlen_bidir_attention_noalloc",
            "fc_probe_kv_stream", "fc_probe_mfma_bf16", "fv_confidence_accept",
-           "fv_fork_view_pages", "fv_commit_accepted")
+           "fv_fork_view_pages", "fv_commit_accepted", "fv_lmhead_workspace_size",
+           "fv_lmhead_verify_accept")
 
 
 class FlashCacheError(RuntimeError):
@@ -62,6 +63,8 @@ _SIGS = {
     "fc_linear_residual": ([P, P, P, I32, I32, I32, I32, P], I32),
     "fc_assemble_query": ([P, P, I32, P, P, I32, P, P], I32),
     "fc_validate_step_inputs": ([P, P, P, I32, I32, I32, P, I32, I32, I32, P], I32),
+    "fv_lmhead_workspace_size": ([I32, I32], SZ),
+    "fv_lmhead_verify_accept": ([P, P, I32, I32, P, I32, I32, P, F32, P, SZ, P, P, P, P, P], I32),
     "fv_fork_view_pages": ([P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, P, P], I32),
     "fv_commit_accepted": ([P, P, P, P, I32, I32, P, P, I32, I32, P, I32, I32, P], I32),
     "fv_confidence_accept": ([P, I32, P, I32, I32, F32, I32, P, P, P, P], I32),
@@ -242,3 +245,17 @@ def fv_commit_accepted(k_cache, v_cache, block_table, view_block_table, max_page
                                    _p(cu_positions), _p(verify_start), B, n_positions,
                                    _p(accept_pos), n_heads, head_dim, _stream(stream))
     _check("fv_commit_accepted", st)
+
+
+def fv_lmhead_workspace_size(R, vocab) -> int:
+    return int(load().fv_lmhead_workspace_size(R, vocab))
+
+
+def fv_lmhead_verify_accept(hidden, w_lm, d_model, vocab, cu_positions, B, R, draft_tokens, tau,
+                            workspace, workspace_bytes, argmax, conf, accept_row, accept_pos,
+                            stream=None):
+    st = load().fv_lmhead_verify_accept(_p(hidden), _p(w_lm), d_model, vocab, _p(cu_positions), B,
+                                        R, _p(draft_tokens), tau, _p(workspace), workspace_bytes,
+                                        _p(argmax), _p(conf), _p(accept_row), _p(accept_pos),
+                                        _stream(stream))
+    _check("fv_lmhead_verify_accept", st)

@@ -392,3 +392,39 @@ class TwoViewVerifyBuffers:
         self.fork(stream)
         self.qkv(stream)
         self.attention(stream)
+
+
+class LMHeadBuffers:
+    """The LM head with the Flash-Verify accept test fused in: final hidden rows
+    of both views times W_lm, reduced per row to argmax and confidence on the
+    device (the logits are never written), then the two-view accept test."""
+
+    def __init__(self, li, device="cuda"):
+        torch = _torch()
+        vi = li.vi
+        cfg = vi.cfg
+        self.li, self.cfg = li, cfg
+        self.R = li.hidden.shape[0]
+        self.n_pos = int(vi.cu_positions[-1])
+        self.hidden = to_device(li.hidden, device)
+        self.w_lm = to_device(li.w_lm, device)
+        self.cu_p = to_device(vi.cu_positions, device)
+        self.draft = to_device(vi.draft, device)
+        ws = fc.fv_lmhead_workspace_size(self.R, cfg.vocab)
+        self.ws_bytes = ws
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        self.argmax = torch.empty(self.R, dtype=torch.int32, device=device)
+        self.conf = torch.empty(self.R, dtype=torch.float32, device=device)
+        self.accept_row = torch.empty(self.R, dtype=torch.uint8, device=device)
+        self.accept_pos = torch.empty(self.n_pos, dtype=torch.uint8, device=device)
+
+    def run(self, stream=None):
+        cfg = self.cfg
+        fc.fv_lmhead_verify_accept(self.hidden, self.w_lm, cfg.d_model, cfg.vocab, self.cu_p,
+                                   cfg.batch, self.R, self.draft, cfg.tau, self.workspace,
+                                   self.ws_bytes, self.argmax, self.conf, self.accept_row,
+                                   self.accept_pos, stream)
+
+    def fetch(self):
+        return dict(argmax=to_host(self.argmax), conf=to_host(self.conf),
+                    accept_row=to_host(self.accept_row), accept_pos=to_host(self.accept_pos))

@@ -345,3 +345,48 @@ def sequence_inputs(inp: StepInputs, b: int, positions: Optional[np.ndarray] = N
                 block_table=np.arange(n_pages, dtype=np.int32)[None, :], pages=pages,
                 cand=inp.cand_mask[int(inp.cu_seqlens_k[b]): int(inp.cu_seqlens_k[b + 1])],
                 q0=q0, q1=q1, L=L)
+
+
+# ---------------------------------------------------------------------------
+# LM-head inputs for the verify-shaped step: the two views' final hidden rows
+# and a vocabulary projection W_lm [vocab, d] ~ N(0, weight_std). At a planted
+# position both view rows are moved along W_lm[t*] so that their logit for t*
+# lands near a target (the same planting recipe as the synthetic logits: the
+# other logits have variance |h|^2 weight_std^2).
+# ---------------------------------------------------------------------------
+
+@dataclass
+class LMHeadInputs:
+    vi: VerifyInputs
+    hidden: np.ndarray          # [R, d] bf16 bits
+    w_lm: np.ndarray            # [V, d] bf16 bits
+
+
+def make_lmhead_inputs(cfg: StepConfig) -> LMHeadInputs:
+    vi = make_verify_inputs(cfg, with_logits=False, with_cache=False)
+    V, d = cfg.vocab, cfg.d_model
+    w = rng_for(cfg.seed, 8).standard_normal(size=(V, d), dtype=np.float32)
+    w *= np.float32(cfg.weight_std)
+    w_bits = to_bf16_bits(w)
+    del w
+    wf = bf16_bits_to_f32(w_bits)
+    h = rng_for(cfg.seed, 9).standard_normal(size=(2 * int(vi.cu_positions[-1]), d),
+                                             dtype=np.float32)
+    crng = rng_for(cfg.seed, 10)
+    c = crng.uniform(0.5, 0.99 - 0.04, size=h.shape[0])
+    c = np.where(c >= cfg.tau - 0.02, c + 0.04, c)
+    sigma2 = d * cfg.weight_std ** 2
+    for b in range(cfg.batch):
+        p0, p1 = int(vi.cu_positions[b]), int(vi.cu_positions[b + 1])
+        n = p1 - p0
+        for i in range(n):
+            p = p0 + i
+            if not vi.planted[p]:
+                continue
+            wt = wf[vi.target[p]].astype(np.float64)
+            for r in (2 * p0 + i, 2 * p0 + n + i):
+                lam = planted_logit(c[r], V, np.sqrt(sigma2))
+                hr = h[r].astype(np.float64)
+                hr += (lam - hr @ wt) * wt / (wt @ wt)
+                h[r] = hr.astype(np.float32)
+    return LMHeadInputs(vi=vi, hidden=to_bf16_bits(h), w_lm=w_bits)

@@ -345,6 +345,50 @@ def verify_accept(logits_bits, cu_positions, draft, tau):
     return am, conf, acc, acc_pos
 
 
+def lmhead_verify_accept(hidden_bits, w_lm_bits, cu_positions, draft, tau, rows=None):
+    """The LM head followed by the accept test over the two views ([NEWS]
+    paragraph 3): logits = hidden . W_lm^T in float64 (no rounding of the
+    logits), then per row the lowest argmax, conf = the largest softmax
+    probability, accept = (argmax == draft) and conf >= tau (float32), and per
+    position the AND of its two view rows. rows: indices of the rows to
+    evaluate (default all; accept_pos is returned only then).
+    Returns (argmax, conf, accept_row[, accept_pos]) for the rows evaluated,
+    plus the top two logits of each (for near-tie bands)."""
+    x = bf16_to_f64(hidden_bits)
+    w = bf16_to_f64(w_lm_bits)
+    R = x.shape[0]
+    sel = np.arange(R) if rows is None else np.asarray(rows, dtype=np.int64)
+    B = len(cu_positions) - 1
+    # row -> verified position index
+    pos_of = np.zeros(R, dtype=np.int64)
+    for b in range(B):
+        p0, p1 = int(cu_positions[b]), int(cu_positions[b + 1])
+        n = p1 - p0
+        pos_of[2 * p0:2 * p0 + n] = np.arange(p0, p1)
+        pos_of[2 * p0 + n:2 * p0 + 2 * n] = np.arange(p0, p1)
+    am = np.zeros(len(sel), dtype=np.int64)
+    conf = np.zeros(len(sel))
+    acc = np.zeros(len(sel), dtype=np.uint8)
+    top2 = np.zeros((len(sel), 2))
+    tau32 = np.float32(tau)
+    for j0 in range(0, len(sel), 64):
+        blk = sel[j0:j0 + 64]
+        logits = x[blk] @ w.T
+        for j, r in enumerate(blk):
+            a, c = argmax_conf(logits[j])
+            am[j0 + j], conf[j0 + j] = a, c
+            acc[j0 + j] = int(a == int(draft[pos_of[r]]) and np.float32(c) >= tau32)
+            top2[j0 + j] = np.sort(logits[j])[-2:][::-1]
+    if rows is not None:
+        return am, conf, acc, top2
+    acc_pos = np.zeros(int(cu_positions[-1]), dtype=np.uint8)
+    for b in range(B):
+        p0, p1 = int(cu_positions[b]), int(cu_positions[b + 1])
+        n = p1 - p0
+        acc_pos[p0:p1] = acc[2 * p0:2 * p0 + n] & acc[2 * p0 + n:2 * p0 + 2 * n]
+    return am, conf, acc, top2, acc_pos
+
+
 def two_view_attention(hidden, w_qkv, n_heads, head_dim, rope_base, k_cache, v_cache,
                        block_table, page_size, cu_positions, verify_start, cache_len, dtype):
     """Flash-Verify's two views with view-private K/V ([NEWS] paragraph 3: drafts

@@ -666,3 +666,31 @@ def test_commit_writes_accepted_draft_rows_only():
     for pg in range(c["kc"].shape[0]):
         if pg not in used:
             np.testing.assert_array_equal(kc2[pg], c["kc"][pg].astype(np.float64))
+
+
+def test_lmhead_oracle_one_hot_rows_match_the_verify_test():
+    """With one-hot hidden rows the logits are exactly a column of W_lm (bf16
+    values), so the LM-head oracle must give the verify oracle's argmax,
+    confidence and flags on those columns taken as logit rows."""
+    rng = np.random.default_rng(51)
+    V, d = 300, 16
+    w = W.to_bf16_bits((rng.standard_normal((V, d)) * 2).astype(np.float32))
+    cu_p = np.array([0, 2, 5], np.int32)
+    R = 2 * 5
+    cols = rng.integers(0, d, size=R)
+    h = np.zeros((R, d), np.float32)
+    h[np.arange(R), cols] = 1.0
+    hb = W.to_bf16_bits(h)
+    logit_bits = np.ascontiguousarray(w[:, cols].T)        # row r = column cols[r] of W
+    draft = rng.integers(0, V, size=5).astype(np.int32)
+    draft[0] = int(np.argmax(O.bf16_to_f64(logit_bits[0])))
+    am, conf, acc, _, acc_pos = O.lmhead_verify_accept(hb, w, cu_p, draft, 0.5)
+    am2, conf2, acc2, acc_pos2 = O.verify_accept(logit_bits, cu_p, draft, 0.5)
+    np.testing.assert_array_equal(am, am2)
+    np.testing.assert_allclose(conf, conf2, rtol=1e-15)
+    np.testing.assert_array_equal(acc, acc2)
+    np.testing.assert_array_equal(acc_pos, acc_pos2)
+    # sampled rows give the same values as the full call
+    am3, conf3, acc3, _ = O.lmhead_verify_accept(hb, w, cu_p, draft, 0.5, rows=[7, 2])
+    np.testing.assert_array_equal(am3, am[[7, 2]])
+    np.testing.assert_array_equal(acc3, acc[[7, 2]])
