@@ -340,6 +340,139 @@ def verify_attention_component(torch, args):
             "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def _timed(torch, stream, fn, args, flush=None, reps=None):
+    """Median of HIP-event intervals of fn on `stream` after a settle phase
+    (the Infinity Cache flushed before each call when `flush` is given)."""
+    import numpy as np
+    reps = reps or args.steps
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s / 2:
+        for _ in range(5):
+            if flush is not None:
+                with torch.cuda.stream(stream):
+                    flush.fill_(5)
+            fn()
+        torch.cuda.synchronize()
+    ts = []
+    for i in range(args.warmup + reps):
+        if flush is not None:
+            with torch.cuda.stream(stream):
+                flush.fill_(5)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        if i >= args.warmup:
+            ts.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+
+
+def verify_views_component(torch, args):
+    """Flash-Verify's two views with view-private K/V on the verify-shaped
+    workload (B=32, 4096-token caches, 16..128 verified positions per sequence,
+    the same draws as the accept test): private pages forked, both views
+    projected into them, each view attending to its own cache, and the commit
+    of a random half of the positions; each stage timed on its own."""
+    import numpy as np
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd import flashcache as fc
+    from kv_cache_attention_step_amd import workload as W
+    cfg = CF.C4
+    dev = "cuda:0"
+    rng = W.rng_for(cfg.seed, 0)
+    W.draw_lengths(cfg, rng)
+    L = np.full(cfg.batch, cfg.cache_len_fixed)
+    table, num_pages = W.draw_paging(cfg, L, rng)
+    n = rng.integers(cfg.verify_len[0], cfg.verify_len[1] + 1, size=cfg.batch)
+    B, H, D, ps, d = cfg.batch, cfg.n_heads, cfg.head_dim, cfg.page_size, cfg.d_model
+    P = int((n.max() + ps - 1) // ps + 1)
+    gen = torch.Generator(device=dev).manual_seed(cfg.seed + 2)
+    total = num_pages + 2 * B * P
+    kc = (torch.randn((total, H, ps, D), generator=gen, device=dev) * cfg.kv_std).to(torch.bfloat16)
+    vc = (torch.randn((total, H, ps, D), generator=gen, device=dev) * cfg.kv_std).to(torch.bfloat16)
+    t32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device=dev)
+    bt, cu_k = t32(table), t32(np.concatenate([[0], np.cumsum(L)]))
+    vs = t32(L - n)
+    cu_p = t32(np.concatenate([[0], np.cumsum(n)]))
+    nv = np.repeat(n, 2)
+    cu_q = t32(np.concatenate([[0], np.cumsum(nv)]))
+    cu_kv = t32(np.concatenate([[0], np.cumsum(np.repeat(L, 2))]))
+    pos = t32(np.concatenate([np.concatenate([np.arange(L[b] - n[b], L[b])] * 2) for b in range(B)]))
+    T_q, T_kv = int(nv.sum()), int(2 * L.sum())
+    hidden = torch.randn((T_q, d), generator=gen, device=dev).to(torch.bfloat16)
+    w = (torch.randn((3 * d, d), generator=gen, device=dev) * cfg.weight_std).to(torch.bfloat16)
+    vt = torch.full((2 * B, table.shape[1]), -1, dtype=torch.int32, device=dev)
+    q_out = torch.empty((T_q, H, D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q_out)
+    qws = fc.fc_qkv_workspace_size(T_q, d, D, fc.FC_DTYPE_BF16)
+    qw = torch.empty(max(qws, 1), dtype=torch.uint8, device=dev)
+    aws = fc.fc_attention_workspace_size(2 * B, T_q, T_kv, H, D, 0)
+    aw = torch.empty(max(aws, 1), dtype=torch.uint8, device=dev)
+    acc = (torch.rand(int(n.sum()), generator=gen, device=dev) < 0.5).to(torch.uint8)
+    stream = torch.cuda.Stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    fork = lambda: fc.fv_fork_view_pages(kc, vc, bt, table.shape[1], ps, cu_k, vs, B, H, D,
+                                         num_pages, P, vt, stream)
+    proj = lambda: fc.fc_qkv_rope_cache_write(hidden, pos, cu_q, 2 * B, T_q, w, d, H, D,
+                                              cfg.rope_base, kc, vc, vt, table.shape[1], ps, q_out,
+                                              None, qw, qws, fc.FC_DTYPE_BF16, stream)
+    attn = lambda: fc.fc_varlen_bidir_attention(q_out, kc, vc, vt, table.shape[1], ps, cu_q, cu_kv,
+                                                2 * B, int(n.max()), T_kv, H, D, 1.0 / D ** 0.5,
+                                                out, None, 0, aw, aws, fc.FC_DTYPE_BF16, stream)
+    commit = lambda: fc.fv_commit_accepted(kc, vc, bt, vt, table.shape[1], ps, cu_p, vs, B,
+                                           int(n.sum()), acc, H, D, stream)
+    fork()
+    res = {"rows": T_q, "positions": int(n.sum()),
+           "fork_us": round(_timed(torch, stream, fork, args, flush), 2),
+           "projection_us": round(_timed(torch, stream, proj, args, flush), 2),
+           "attention_us": round(_timed(torch, stream, attn, args, flush), 2),
+           "commit_us": round(_timed(torch, stream, commit, args, flush), 2)}
+    kv_bytes = 2.0 * 2 * L.sum() * H * D * 2            # each view streams its sequence's K and V
+    res["attention_gbs"] = round((kv_bytes + 2.0 * T_q * d * 2) / (res["attention_us"] * 1e-6) / 1e9, 1)
+    res["projection_tflops"] = round(2.0 * T_q * 3 * d * d / (res["projection_us"] * 1e-6) / 1e12, 1)
+    del kc, vc
+    return res
+
+
+def lmhead_component(torch, args):
+    """The LM head with the fused accept test on the verify-shaped rows (4366
+    rows of d 4096 against a 126464-token vocabulary); dense bf16 MFMA work
+    2 R V d, reported against the MFMA roofline."""
+    import numpy as np
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd import flashcache as fc
+    from kv_cache_attention_step_amd import workload as W
+    cfg = CF.C4
+    dev = "cuda:0"
+    rng = W.rng_for(cfg.seed, 0)
+    W.draw_lengths(cfg, rng)
+    W.draw_paging(cfg, np.full(cfg.batch, cfg.cache_len_fixed), rng)
+    n = rng.integers(cfg.verify_len[0], cfg.verify_len[1] + 1, size=cfg.batch)
+    R = int(2 * n.sum())
+    gen = torch.Generator(device=dev).manual_seed(cfg.seed + 3)
+    h = torch.randn((R, cfg.d_model), generator=gen, device=dev).to(torch.bfloat16)
+    w = (torch.randn((cfg.vocab, cfg.d_model), generator=gen, device=dev) * cfg.weight_std).to(torch.bfloat16)
+    cu_p = torch.tensor(np.concatenate([[0], np.cumsum(n)]), dtype=torch.int32, device=dev)
+    draft = torch.randint(0, cfg.vocab, (int(n.sum()),), generator=gen, device=dev, dtype=torch.int32)
+    wsb = fc.fv_lmhead_workspace_size(R, cfg.vocab)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    am = torch.empty(R, dtype=torch.int32, device=dev)
+    cf = torch.empty(R, dtype=torch.float32, device=dev)
+    ar = torch.empty(R, dtype=torch.uint8, device=dev)
+    ap = torch.empty(int(n.sum()), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    fn = lambda: fc.fv_lmhead_verify_accept(h, w, cfg.d_model, cfg.vocab, cu_p, cfg.batch, R,
+                                            draft, cfg.tau, ws, wsb, am, cf, ar, ap, stream)
+    us = _timed(torch, stream, fn, args, None, reps=max(5, args.steps // 5))
+    flops = 2.0 * R * cfg.vocab * cfg.d_model
+    tf = flops / (us * 1e-6) / 1e12
+    del w
+    return {"rows": R, "vocab": cfg.vocab, "avg_us": round(us, 1), "achieved_tflops": round(tf, 1),
+            "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "logits_bytes_not_written": R * cfg.vocab * 2}
+
+
 def stack_main(args):
     """Layer-stack workload: 32 layers x 32 block-wise denoising steps of one
     512-token generation (B=32). Prints one JSON line with the time per denoising
@@ -505,6 +638,8 @@ def main():
                 "frac_of_measured_peak": kd.get("frac_of_measured_stream")}
     verify = None if args.no_verify else verify_component(torch, args)
     verify_attn = None if args.no_verify else verify_attention_component(torch, args)
+    verify_views = None if args.no_verify else verify_views_component(torch, args)
+    lmhead = None if args.no_verify else lmhead_component(torch, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seqs, args.cpu_budget_s)
@@ -536,6 +671,8 @@ def main():
                    "ms_per_step_mean": round(float(step_ms.mean()), 4)},
         "verify_accept_c4": verify,
         "verify_attention_c4": verify_attn,
+        "verify_two_views_c4": verify_views,
+        "lmhead_verify_c4": lmhead,
         "settle": {"seconds": args.settle_s, "steps": settle_steps},
         "step_ms_min": round(float(step_ms.min()), 4),
         "wall_s_timed_loop": round(wall, 4),

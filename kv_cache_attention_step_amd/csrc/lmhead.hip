@@ -9,8 +9,9 @@
 // forum post, section 4); the predictions come from the model's logits.
 //
 // The GEMM is the projection's tile pipeline (gemm_tile.hpp, Gemm8 with
-// 256-row tiles, persistent over the tiles, column tile fastest so each XCD
-// streams a disjoint slice of W). Epilogue per tile: each wave holds 64 rows x
+// 256-row tiles, persistent over the tiles; each XCD takes whole 256-column
+// blocks of W and runs every row tile of a block before the next, so W is
+// streamed from memory once). Epilogue per tile: each wave holds 64 rows x
 // 128 vocabulary columns as fp32 accumulators; per row it reduces them to
 // (max m, lowest column holding m, sum of exp(x - m)) across its 32 lanes
 // with butterfly exchanges and writes that partial. A second kernel merges the
@@ -39,17 +40,34 @@ __global__ __launch_bounds__(Gemm8<256>::THREADS, 1) void lmhead_partials(
   const int wm = wave >> 1, wn = wave & 1;
   const int N = n_tiles_n * G::BN;
   const int n_part = 2 * n_tiles_n;
-  int tile = blockIdx.x;
-  G::prologue(hidden, d, M, w, d, N, d, (tile / n_tiles_n) * G::BM, (tile % n_tiles_n) * G::BN, sts);
+  // Tile order. W (vocab x d) is far larger than the Infinity Cache, so each
+  // 256-column block of it must be streamed once and then serve every row
+  // tile from L2: workgroup g (placed on XCD g mod 8) walks the column blocks
+  // nt = g mod 8, + 8, ... of that XCD, all row tiles of one block before the
+  // next, row tile fastest. Any placement gives the same result.
+  const int n_tiles_m = n_tiles / n_tiles_n;
+  const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;   // gridDim.x is a multiple of 8
+  const int n_blk = (n_tiles_n - xcd + 7) >> 3;                  // column blocks of this XCD
+  const int my_tiles = n_blk * n_tiles_m;
+  int j = blockIdx.x >> 3;
+  if (j >= my_tiles) return;
+  auto coords = [&](int jj, int& mt, int& nt) {
+    mt = jj % n_tiles_m;
+    nt = xcd + 8 * (jj / n_tiles_m);
+  };
+  int mt, nt;
+  coords(j, mt, nt);
+  G::prologue(hidden, d, M, w, d, N, d, mt * G::BM, nt * G::BN, sts);
   for (;;) {
-    const int nt = tile % n_tiles_n, mt = tile / n_tiles_n;
     const int m0 = mt * G::BM, n0 = nt * G::BN;
     f32x16_t acc[G::MB][G::NB];
     G::template main_loop<true>(hidden, d, M, w, d, N, d, m0, n0, sts, acc);
-    const int next = tile + gridDim.x;
-    if (next < n_tiles)
-      G::prologue(hidden, d, M, w, d, N, d, (next / n_tiles_n) * G::BM, (next % n_tiles_n) * G::BN,
-                  sts);
+    const int jn = j + per_xcd;
+    int mt_n = 0, nt_n = 0;
+    if (jn < my_tiles) {
+      coords(jn, mt_n, nt_n);
+      G::prologue(hidden, d, M, w, d, N, d, mt_n * G::BM, nt_n * G::BN, sts);
+    }
     const int col0 = n0 + wn * 128;
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb) {
@@ -84,8 +102,10 @@ __global__ __launch_bounds__(Gemm8<256>::THREADS, 1) void lmhead_partials(
         if (lr == 0 && row < M) part[(size_t)row * n_part + nt * 2 + wn] = Part{m, s, idx};
       }
     }
-    tile = next;
-    if (tile >= n_tiles) break;
+    j = jn;
+    if (j >= my_tiles) break;
+    mt = mt_n;
+    nt = nt_n;
   }
 }
 
@@ -208,7 +228,9 @@ extern "C" fc_status_t fv_lmhead_verify_accept(const void* hidden, const void* w
   }
   const int n_tiles_n = vocab / 256;
   const int n_tiles = ((R + 255) / 256) * n_tiles_n;
-  const int grid = n_tiles < fc_num_cus() ? n_tiles : fc_num_cus();
+  // persistent: one workgroup per CU (a multiple of 8, the XCD count), each
+  // walking its XCD's column blocks; workgroups beyond an XCD's tiles exit
+  const int grid = fc_num_cus() >= 8 ? fc_num_cus() / 8 * 8 : 8;
   hipLaunchKernelGGL(lmhead_partials, dim3(grid), dim3(Gemm8<256>::THREADS), 0, st,
                      (const uint16_t*)hidden, R, (const uint16_t*)w_lm, d_model, n_tiles_n, n_tiles,
                      (Part*)workspace);

@@ -588,3 +588,18 @@ def test_verify_argmax_ties_and_vocab_edges(torch_cuda):
         assert np.array_equal(got[2][~near], acc[~near])
         if not near.any():
             assert np.array_equal(got[3], acc_pos)
+
+
+@pytest.mark.parametrize("batch,q_per_seq", [(64, 128), (8, 256), (8, 512)])
+def test_sweep_shapes(torch_cuda, batch, q_per_seq):
+    """The shapes the throughput sweeps add beyond C2: 64 sequences (more than
+    one wave of sequences: the longest-first order comes from its own kernel),
+    and 256 or 512 query rows per sequence (the importance path walks two or
+    four 128-row tiles per (sequence, head)); every output of every sequence
+    against the oracle."""
+    _say(f"case sweep shape B={batch}, {q_per_seq} query rows per sequence")
+    cfg = dataclasses.replace(CF.C2, name=f"sweep-{batch}x{q_per_seq}", seed=90 + batch + q_per_seq,
+                              batch=batch, window=q_per_seq // 2, track=q_per_seq // 2)
+    inp = W.make_step_inputs(cfg)
+    got = run_gpu_step(inp, torch_cuda)
+    full_parity(inp, got)
