@@ -55,6 +55,9 @@ def parse():
                     help="instead of the benchmark line: step throughput of the C2 layer "
                          "over batch sizes 1..64 (query 64 window + 64 tracked) or over query "
                          "lengths 32..512 per sequence (B=32); one JSON line per point")
+    ap.add_argument("--only", choices=tuple(COMPONENTS), default=None,
+                    help="run only this verify-shaped component and print its JSON object "
+                         "(for per-component counter runs; not the benchmark line)")
     return ap.parse_args()
 
 
@@ -515,12 +518,39 @@ def stack_main(args):
     print(json.dumps(out), flush=True)
 
 
+def calibration_copy(torch):
+    """One 256 MiB device copy and one 512 MiB fill: the references the HBM
+    read and write byte counters are scaled by."""
+    src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    fill = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    fill.fill_(1)
+    torch.cuda.synchronize()
+    del fill
+
+
+COMPONENTS = {"verify": "verify_component", "verify_attention": "verify_attention_component",
+              "views": "verify_views_component", "lmhead": "lmhead_component"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.only:
+        import torch
+        torch.cuda.set_device(0)
+        if args.calib:
+            calibration_copy(torch)
+        res = globals()[COMPONENTS[args.only]](torch, args)
+        print(json.dumps({"component": args.only, **res}), flush=True)
+        return
     if args.sweep:
         return sweep_main(args)
     if args.config == "C3":
@@ -558,12 +588,7 @@ def main():
             ev[4].record(stream)
 
     if args.calib:
-        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch)
     # settle: the clocks swing for the first tens of milliseconds of sustained load
     t_settle = time.perf_counter()
     settle_steps = 0

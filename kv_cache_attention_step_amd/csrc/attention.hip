@@ -49,11 +49,17 @@ constexpr int A_STAGE = K_TILE + V_TILE;
 constexpr int A_RED = 2 * 4 * AKT * 4;  // double-buffered [wave][key] fp32 partial sums
 constexpr int A_LDS = 2 * A_STAGE + A_RED;
 constexpr float LOG2E = 1.4426950408889634f;
-// Cache policy of the K/V stream loads: nontemporal. Every (page, head) block is
-// consumed once per pass and is too far from its re-read to be kept; with the
-// default policy the paged stream saturates near half the HBM rate that the
-// nontemporal policy reaches for the same addresses.
+// Cache policy of the K/V stream loads of the importance path: nontemporal.
+// Every (page, head) block is consumed once per pass and is too far from its
+// re-read to be kept; with the default policy the paged stream saturates near
+// half the HBM rate that the nontemporal policy reaches for the same addresses.
 constexpr int KV_POLICY = 2;
+// The one-pass path keeps the default policy: there the same blocks are read
+// again within microseconds by a neighbouring workgroup on the same XCD (the
+// second row tile of a (sequence, head), or the other view of a sequence whose
+// view-private page table shares the prefix), and the nontemporal policy
+// evicts them from L2 before that read.
+constexpr int KV_POLICY_SHARED = 0;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -102,7 +108,7 @@ struct TileRegs {
   u32x4_t v[4];
 };
 
-template <bool PS_GE16, bool WANT_V>
+template <bool PS_GE16, bool WANT_V, int POL = KV_POLICY>
 FC_DEVICE void load_group(const AttnArgs& a, const int32_t* __restrict__ bt, int h, int tile, int L,
                           int g, int lane, TileRegs& r) {
   const int key0 = tile * AKT + g * 16;
@@ -123,12 +129,12 @@ FC_DEVICE void load_group(const AttnArgs& a, const int32_t* __restrict__ bt, int
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc + base, bytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((lane >> 4) + 4 * i) * (AD * 2) + (lane & 15) * 16, 0, KV_POLICY);
+      r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((lane >> 4) + 4 * i) * (AD * 2) + (lane & 15) * 16, 0, POL);
     if (WANT_V) {
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vc + base, bytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((lane >> 4) + 4 * i) * (AD * 2) + (lane & 15) * 16, 0, KV_POLICY);
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((lane >> 4) + 4 * i) * (AD * 2) + (lane & 15) * 16, 0, POL);
     }
   } else {
 #pragma unroll
@@ -485,12 +491,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
     } else {
       // ---------------- single pass, online softmax ----------------
       float m = -INFINITY, l = 0.f;
-      load_group<PS_GE16, true>(a, bt, h, 0, L, wave, lane, tr);
+      load_group<PS_GE16, true, KV_POLICY_SHARED>(a, bt, h, 0, L, wave, lane, tr);
       store_group<true>(lds, wave, lane, tr);
       __syncthreads();
       for (int tile = 0; tile < n_tiles; ++tile) {
         const bool more = tile + 1 < n_tiles;
-        load_group<PS_GE16, true>(a, bt, h, tile + 1, L, wave, lane, tr);
+        load_group<PS_GE16, true, KV_POLICY_SHARED>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
         const char* vs = ks + K_TILE;
         const int kb0 = KS ? kbw : 0;

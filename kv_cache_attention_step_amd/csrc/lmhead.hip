@@ -22,6 +22,10 @@
 namespace {
 
 constexpr float LOG2E_L = 1.4426950408889634f;
+// column blocks of W an XCD's workgroups share at one time (tile order below):
+// at 4366 rows x 126464 columns, 1, 2, 4, 8, 16 and 32 give 4237-4324, 4188,
+// 4108, 3998-4190, 4386 and 5175 us in one A/B run
+constexpr int LMHEAD_COL_GROUP = 8;
 
 struct Part {
   float m, s;
@@ -30,7 +34,7 @@ struct Part {
 
 __global__ __launch_bounds__(Gemm8<256>::THREADS, 1) void lmhead_partials(
     const uint16_t* __restrict__ hidden, int M, const uint16_t* __restrict__ w, int d,
-    int n_tiles_n, int n_tiles, Part* __restrict__ part) {
+    int n_tiles_n, int n_tiles, int grp, Part* __restrict__ part) {
   using G = Gemm8<256>;
   __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
@@ -43,17 +47,22 @@ __global__ __launch_bounds__(Gemm8<256>::THREADS, 1) void lmhead_partials(
   // Tile order. W (vocab x d) is far larger than the Infinity Cache, so each
   // 256-column block of it must be streamed once and then serve every row
   // tile from L2: workgroup g (placed on XCD g mod 8) walks the column blocks
-  // nt = g mod 8, + 8, ... of that XCD, all row tiles of one block before the
-  // next, row tile fastest. Any placement gives the same result.
+  // nt = g mod 8, + 8, ... of that XCD in groups of `grp` blocks, all row tiles
+  // of one group before the next, the group's blocks fastest: the tiles an
+  // XCD runs at one time then share grp blocks of W and few row blocks of the
+  // hidden states. Any placement gives the same result.
   const int n_tiles_m = n_tiles / n_tiles_n;
   const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;   // gridDim.x is a multiple of 8
   const int n_blk = (n_tiles_n - xcd + 7) >> 3;                  // column blocks of this XCD
   const int my_tiles = n_blk * n_tiles_m;
   int j = blockIdx.x >> 3;
   if (j >= my_tiles) return;
+  const int per_grp = grp * n_tiles_m;
   auto coords = [&](int jj, int& mt, int& nt) {
-    mt = jj % n_tiles_m;
-    nt = xcd + 8 * (jj / n_tiles_m);
+    const int g = jj / per_grp, r = jj - g * per_grp;
+    const int gsz = min(grp, n_blk - g * grp);   // the last group may be smaller
+    mt = r / gsz;
+    nt = xcd + 8 * (g * grp + r % gsz);
   };
   int mt, nt;
   coords(j, mt, nt);
@@ -233,7 +242,7 @@ extern "C" fc_status_t fv_lmhead_verify_accept(const void* hidden, const void* w
   const int grid = fc_num_cus() >= 8 ? fc_num_cus() / 8 * 8 : 8;
   hipLaunchKernelGGL(lmhead_partials, dim3(grid), dim3(Gemm8<256>::THREADS), 0, st,
                      (const uint16_t*)hidden, R, (const uint16_t*)w_lm, d_model, n_tiles_n, n_tiles,
-                     (Part*)workspace);
+                     LMHEAD_COL_GROUP, (Part*)workspace);
   fc_status_t s = fc_check_launch("fv_lmhead_verify_accept");
   if (s != FC_OK) return s;
   hipLaunchKernelGGL(lmhead_finish, dim3(R), dim3(256), 0, st, (const Part*)workspace,

@@ -8,13 +8,20 @@ with --calib copies a 256 MiB buffer once (read 256 MiB, write 256 MiB), and
 the Infinity-Cache flush between steps fills a 512 MiB buffer (write 512 MiB).
 
     python -m kv_cache_attention_step_amd.profiling traffic FETCH_DIR WRITE_DIR OUT_JSON
+    python -m kv_cache_attention_step_amd.profiling traffic-multi OUT_JSON LABEL=FETCH_DIR,WRITE_DIR ...
     python -m kv_cache_attention_step_amd.profiling stats KERNEL_STATS_CSV
+    python -m kv_cache_attention_step_amd.profiling mfma COUNTER_DIR N_SIMD N_XCD
 
 FETCH_DIR / WRITE_DIR hold the rocprofv3 csv output (*counter_collection.csv).
 OUT_JSON records the per-dispatch averages, the calibration factors and a
 SHA-256 of the kernel sources the counters were taken on; bench.py reports the
-traffic only while those sources are unchanged. `stats` prints the kernel
-table of a `rocprofv3 --kernel-trace --stats` run as markdown.
+traffic only while those sources are unchanged. traffic-multi does the same for
+several labelled runs (one bench component each, every run calibrated by its
+own copy and fill); kernels of the run labelled "step" keep their plain names,
+the others are stored as LABEL:name. `stats` prints the kernel table of a
+`rocprofv3 --kernel-trace --stats` run as markdown. `mfma` prints, per kernel,
+the matrix-unit busy fraction, the bf16 MFMA work, the LDS instructions and the
+clock (one XCD's busy clocks over the dispatch's duration) per dispatch.
 """
 import csv
 import glob
@@ -29,8 +36,14 @@ CSRC = os.path.join(HERE, "csrc")
 # kernel of each step component, as rocprofv3 names it (substring match)
 KERNELS = {
     "qkv_rope_cache_write": "qkv_rope_cache_bf16_d128",
-    "varlen_bidir_attention": "attn_bf16_d128",
+    "varlen_bidir_attention": "attn_bf16_d128<true",
+    "attention_one_pass": "attn_bf16_d128<false",
     "importance_topk": "topk_kernel",
+    "verify_rows": "verify_rows",
+    "lmhead_partials": "lmhead_partials",
+    "fork_view_pages": "fork_kernel",
+    "commit_accepted": "commit_kernel",
+    "linear_residual": "linear_residual_dma",
 }
 CALIB_COPY_KIB = 256 * 1024   # the --calib copy: reads and writes this much
 CALIB_FILL_KIB = 512 * 1024   # the flush fill: writes this much
@@ -71,7 +84,8 @@ def summarize(fetch_dir: str, write_dir: str):
     fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
     write = per_dispatch(write_dir, "WRITE_SIZE")
     # calibration: the largest copy dispatch (FETCH) and the largest fill (WRITE)
-    copies = [v for (n, v) in fetch.values() if "copy" in n.lower()]
+    # the --calib device copy (a blit kernel; other copy kernels convert dtypes)
+    copies = [v for (n, v) in fetch.values() if "copybuffer" in n.lower()]
     fills = [v for (n, v) in write.values() if "fill" in n.lower()]
     if not copies or not fills:
         raise RuntimeError("calibration dispatches not found (run the bench with --calib)")
@@ -91,6 +105,55 @@ def summarize(fetch_dir: str, write_dir: str):
                             "fill_write_kib": round(max(fills), 1),
                             "fetch_factor": round(f_fetch, 5), "write_factor": round(f_write, 5)},
             "kernels": kernels, "sources_sha256": sources_digest()}
+
+
+def summarize_multi(pairs):
+    """pairs: [(label, fetch_dir, write_dir)]; one record with every labelled
+    run's kernels (label "step" unprefixed) and its calibration."""
+    out = {"calibration": {}, "kernels": {}, "sources_sha256": sources_digest()}
+    for label, fd, wd in pairs:
+        rec = summarize(fd, wd)
+        out["calibration"][label] = rec["calibration"]
+        for k, v in rec["kernels"].items():
+            out["kernels"][k if label == "step" else f"{label}:{k}"] = v
+    return out
+
+
+def mfma_summary(csv_dir: str, n_simd: int, n_xcd: int):
+    """{kernel: dict(dispatches, mfma_busy, bf16_mfma_flops, lds_insts, clock_ghz, us)}
+    averaged over dispatches. rocprofv3 reports each counter summed over its
+    hardware instances: SQ counters over every SIMD's sequencer, GRBM_GUI_ACTIVE
+    over the XCDs (each counts its own busy clocks), so one XCD's busy clocks
+    are GRBM_GUI_ACTIVE / n_xcd and the matrix-unit busy fraction is
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / n_xcd x n_simd)."""
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {csv_dir}")
+    disp = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (f, r["Dispatch_Id"])
+            d = disp.setdefault(key, {"name": r["Kernel_Name"],
+                                      "ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+            c = r["Counter_Name"]
+            d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for key, sub in KERNELS.items():
+        ds = [d for d in disp.values() if sub in d["name"] and d.get("GRBM_GUI_ACTIVE")]
+        if not ds:
+            continue
+        mean = lambda f: sum(f(d) for d in ds) / len(ds)
+        xcd_clocks = lambda d: d["GRBM_GUI_ACTIVE"] / n_xcd
+        out[key] = {
+            "dispatches": len(ds),
+            "mfma_busy": round(mean(lambda d: d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) /
+                                    (xcd_clocks(d) * n_simd)), 4),
+            "bf16_mfma_flops": mean(lambda d: d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512),
+            "lds_insts": mean(lambda d: d.get("SQ_INSTS_LDS", 0.0)),
+            "lds_bank_conflict_cycles": mean(lambda d: d.get("SQ_LDS_BANK_CONFLICT", 0.0)),
+            "clock_ghz": round(mean(lambda d: xcd_clocks(d) / d["ns"] if d["ns"] > 0 else 0.0), 3),
+            "us": round(mean(lambda d: d["ns"] * 1e-3), 2)}
+    return out
 
 
 def load_traffic(path: str, kernel: str):
@@ -133,7 +196,21 @@ if __name__ == "__main__":
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(json.dumps(rec, indent=1))
+    elif len(sys.argv) >= 4 and sys.argv[1] == "traffic-multi":
+        pairs = []
+        for arg in sys.argv[3:]:
+            label, dirs = arg.split("=", 1)
+            fd, wd = dirs.split(",")
+            pairs.append((label, fd, wd))
+        rec = summarize_multi(pairs)
+        with open(sys.argv[2], "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec, indent=1))
     elif len(sys.argv) == 3 and sys.argv[1] == "stats":
         print(stats_markdown(sys.argv[2]))
+    elif len(sys.argv) == 5 and sys.argv[1] == "mfma":
+        for k, v in mfma_summary(sys.argv[2], int(sys.argv[3]), int(sys.argv[4])).items():
+            print(k, json.dumps(v))
     else:
         sys.exit(__doc__)

@@ -37,7 +37,15 @@ Where the pages are silent the oracle takes these readings:
     softmax probability; accept a row when argmax == draft and conf >= tau (both
     as float32); a position is accepted when both of its view rows are.
   * confidence-aware acceptance: a position is accepted when its confidence
-    alone reaches tau; optionally at least the most confident one per sequence.
+    alone reaches tau; optionally at least the most confident one per sequence
+    (the lowest position among equally confident rows).
+  * two views: each view projects its own hidden rows at the verified
+    positions; a view attends to the shared cache with its own fresh K/V in
+    place of the verified block (nothing of the other view), one-pass softmax.
+  * commit: for every accepted position the draft view's K/V (rounded to the
+    cache's dtype) replaces the shared cache entry; all else is untouched.
+  * LM head: logits = h W_lm^T in float64 from the bf16 operands, never rounded
+    to bf16; argmax, confidence and the accept test as for verify.
 """
 import math
 from itertools import combinations

@@ -63,3 +63,27 @@ def test_stats_markdown(tmp_path):
     md = P.stats_markdown(str(f)).splitlines()
     assert md[2].startswith("| `attn_bf16_d128<true, true>` | 3 | 200.0 |")
     assert md[3].startswith("| `topk_kernel` | 3 | 20.0 |")
+
+
+def test_mfma_summary_busy_fraction(tmp_path):
+    d = tmp_path / "m"
+    os.makedirs(d)
+    qkv = "void (anonymous namespace)::qkv_rope_cache_bf16_d128<Gemm8<256>, true>(int)"
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        # 2 XCDs, 8 SIMDs: GRBM_GUI_ACTIVE is summed over the XCDs (2 x 100 clocks
+        # in 50 ns: 2 GHz), SQ counters over the SIMDs
+        for disp, busy in ((1, 600.0), (2, 200.0)):
+            row = {"Dispatch_Id": disp, "Kernel_Name": qkv, "Start_Timestamp": 1000,
+                   "End_Timestamp": 1050}
+            w.writerow({**row, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES", "Counter_Value": busy})
+            w.writerow({**row, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 200.0})
+            w.writerow({**row, "Counter_Name": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "Counter_Value": 2.0})
+    rec = P.mfma_summary(str(d), n_simd=8, n_xcd=2)
+    k = rec["qkv_rope_cache_write"]
+    assert k["dispatches"] == 2
+    assert abs(k["mfma_busy"] - (600 / 800 + 200 / 800) / 2) < 1e-12
+    assert k["bf16_mfma_flops"] == 1024.0
+    assert k["clock_ghz"] == 2.0 and k["us"] == 0.05
