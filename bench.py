@@ -84,17 +84,17 @@ def sweep_main(args):
         inp = W.make_step_inputs(cfg)
         bufs = StepBuffers(inp, device="cuda:0")
 
-        def one_step(ev=None):
+        def one_step(ev=None, split=False):
             with torch.cuda.stream(stream):
                 flush.fill_(1)
             if ev is not None:
                 ev[0].record(stream)
             bufs.assemble(stream)
             bufs.qkv(stream)
-            if ev is not None:
+            if split:
                 ev[1].record(stream)
             bufs.attention(stream)
-            if ev is not None:
+            if split:
                 ev[2].record(stream)
             bufs.topk(stream)
             if ev is not None:
@@ -106,12 +106,15 @@ def sweep_main(args):
             torch.cuda.synchronize()
         for _ in range(args.warmup):
             one_step()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            one_step(evs[i])
+        mk = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        evs_step, evs = mk(), mk()
+        for i in range(args.steps):      # step time: events at the step boundaries only
+            one_step(evs_step[i])
+        for i in range(args.steps):      # kernel intervals: events between the kernels
+            one_step(evs[i], split=True)
         torch.cuda.synchronize()
-        el = lambda a, b: float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
-        ms = el(0, 3)
+        el = lambda a, b, e_=None: float(np.mean([e[a].elapsed_time(e[b]) for e in (e_ or evs)]))
+        ms = el(0, 3, evs_step)
         print(json.dumps({"sweep": args.sweep, "batch": inp.B, "query_per_seq": cfg.window + cfg.track,
                           "query_tokens": inp.T_q, "cache_tokens": inp.T_k,
                           "ms_per_step": round(ms, 4),
@@ -225,6 +228,13 @@ def measured_peaks(torch, bufs, flush, stream, reps=20):
             "kv_bytes": kv_bytes}
 
 
+def _traffic(name):
+    """HBM bytes per launch of a kernel from the committed counter runs (None once
+    the kernel sources differ from those the counters were taken on)."""
+    from kv_cache_attention_step_amd.profiling import load_traffic
+    return load_traffic(TRAFFIC_FILE, name)
+
+
 def verify_component(torch, args):
     """The Flash-Verify accept test at the verify-shaped workload (B=32, 16..128
     verified positions per sequence, two views, vocab 126464): logits drawn on the
@@ -276,7 +286,8 @@ def verify_component(torch, args):
     return {"rows": R, "vocab": cfg.vocab, "avg_us": round(us, 2),
             "rows_per_s": round(R / (us * 1e-6), 1),
             "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic_bytes": _traffic("verify:verify_rows")}
 
 
 def verify_attention_component(torch, args):
@@ -340,7 +351,8 @@ def verify_attention_component(torch, args):
     del kc, vc
     return {"query_rows": T_q, "cache_tokens": T_k, "avg_us": round(us, 2),
             "algorithmic_bytes": nbytes, "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic_bytes": _traffic("verify_attention:attention_one_pass")}
 
 
 def _timed(torch, stream, fn, args, flush=None, reps=None):
@@ -431,8 +443,14 @@ def verify_views_component(torch, args):
            "projection_us": round(_timed(torch, stream, proj, args, flush), 2),
            "attention_us": round(_timed(torch, stream, attn, args, flush), 2),
            "commit_us": round(_timed(torch, stream, commit, args, flush), 2)}
-    kv_bytes = 2.0 * 2 * L.sum() * H * D * 2            # each view streams its sequence's K and V
-    res["attention_gbs"] = round((kv_bytes + 2.0 * T_q * d * 2) / (res["attention_us"] * 1e-6) / 1e9, 1)
+    # algorithmic bytes: the pages before a sequence's first private page once, each
+    # view's private pages (from that page to the end) once per view, q and out
+    first = (L - n) // ps * ps
+    uniq = (first.sum() + 2 * (L - first).sum()) * H * D * 2 * 2 + 2.0 * T_q * d * 2
+    res["attention_algorithmic_bytes"] = float(uniq)
+    res["attention_gbs"] = round(uniq / (res["attention_us"] * 1e-6) / 1e9, 1)
+    res["attention_frac_hbm"] = round(uniq / (res["attention_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    res["attention_traffic_bytes"] = _traffic("views:attention_one_pass")
     res["projection_tflops"] = round(2.0 * T_q * 3 * d * d / (res["projection_us"] * 1e-6) / 1e12, 1)
     del kc, vc
     return res
@@ -473,7 +491,8 @@ def lmhead_component(torch, args):
     del w
     return {"rows": R, "vocab": cfg.vocab, "avg_us": round(us, 1), "achieved_tflops": round(tf, 1),
             "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "logits_bytes_not_written": R * cfg.vocab * 2}
+            "logits_bytes_not_written": R * cfg.vocab * 2,
+            "traffic_bytes": _traffic("lmhead:lmhead_partials")}
 
 
 def stack_main(args):
@@ -568,20 +587,23 @@ def main():
     stream = torch.cuda.Stream()
     flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
 
-    def one_step(ev=None):
+    def one_step(ev=None, split=False):
+        """One step; events at its boundaries, and between its kernels when split
+        (each event record between two kernels adds a ~5 us gap on the GPU, so
+        the step time is taken from steps without them)."""
         if flush is not None:
             with torch.cuda.stream(stream):
                 flush.fill_(1)
         if ev is not None:
             ev[0].record(stream)
         bufs.assemble(stream)
-        if ev is not None:
+        if split:
             ev[1].record(stream)
         bufs.qkv(stream)
-        if ev is not None:
+        if split:
             ev[2].record(stream)
         bufs.attention(stream)
-        if ev is not None:
+        if split:
             ev[3].record(stream)
         bufs.topk(stream)
         if ev is not None:
@@ -600,16 +622,24 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    mk = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # the timed steps: events only at each step's boundaries
+    evs_step = mk()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(evs[i])
+        one_step(evs_step[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    seg = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in evs]) * 1e3   # us
+    # the same number of steps again with events between the kernels, for the
+    # per-kernel intervals
+    evs = mk()
+    for i in range(args.steps):
+        one_step(evs[i], split=True)
+    torch.cuda.synchronize()
+    seg = lambda a, b, e_=None: np.array([e[a].elapsed_time(e[b]) for e in (e_ or evs)]) * 1e3  # us
     k0, k1, k2, k3 = seg(0, 1), seg(1, 2), seg(2, 3), seg(3, 4)
-    step_ms = seg(0, 4) * 1e-3
+    step_ms = seg(0, 4, evs_step) * 1e-3
     ms_per_step = float(np.median(step_ms))
     work = step_work(inp)
     peaks = None if args.no_probes else measured_peaks(torch, bufs, flush, stream)
@@ -691,9 +721,11 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "measured_peaks": peaks,
-        "timing": {"statistic": "median of the timed steps' HIP-event intervals (kernel "
-                                "entries: mean and median)",
-                   "ms_per_step_mean": round(float(step_ms.mean()), 4)},
+        "timing": {"statistic": "median of the timed steps' HIP-event intervals, events at "
+                                "step boundaries only; kernel entries (mean and median) from "
+                                "a second run of as many steps with events between kernels",
+                   "ms_per_step_mean": round(float(step_ms.mean()), 4),
+                   "ms_per_step_with_kernel_events": round(float(np.median(seg(0, 4))) * 1e-3, 4)},
         "verify_accept_c4": verify,
         "verify_attention_c4": verify_attn,
         "verify_two_views_c4": verify_views,
