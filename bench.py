@@ -319,7 +319,7 @@ def verify_attention_component(torch, args):
     vc = (torch.randn((num_pages, H, ps, D), generator=gen, device=dev) * cfg.kv_std).to(torch.bfloat16)
     q = torch.randn((T_q, H, D), generator=gen, device=dev).to(torch.bfloat16)
     out = torch.empty_like(q)
-    wsb = fc.fc_attention_workspace_size(B, T_q, T_k, H, D, 0)
+    wsb = fc.fc_attention_workspace_size(B, T_q, T_k, H, D, 0, int(Qb.max()))
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -422,7 +422,7 @@ def verify_views_component(torch, args):
     out = torch.empty_like(q_out)
     qws = fc.fc_qkv_workspace_size(T_q, d, D, fc.FC_DTYPE_BF16)
     qw = torch.empty(max(qws, 1), dtype=torch.uint8, device=dev)
-    aws = fc.fc_attention_workspace_size(2 * B, T_q, T_kv, H, D, 0)
+    aws = fc.fc_attention_workspace_size(2 * B, T_q, T_kv, H, D, 0, int(n.max()))
     aw = torch.empty(max(aws, 1), dtype=torch.uint8, device=dev)
     acc = (torch.rand(int(n.sum()), generator=gen, device=dev) < 0.5).to(torch.uint8)
     stream = torch.cuda.Stream()

@@ -148,9 +148,13 @@ fc_status_t fc_qkv_rope_cache_write(
 size_t fc_qkv_workspace_size(int32_t T_q, int32_t d_model, int32_t head_dim, int32_t dtype);
 
 /* Bytes of device workspace fc_varlen_bidir_attention needs for these sizes
- * (0 when none). */
+ * (0 when none). max_seqlen_q: the largest query length of any sequence in the
+ * calls the workspace serves (with importance, sequences of more than 128 query
+ * rows need (ceil(max_seqlen_q / 128) - 1) * n_heads * T_k floats more). A
+ * workspace sized for the largest B, T_k and max_seqlen_q serves smaller calls. */
 size_t fc_attention_workspace_size(int32_t B, int32_t T_q, int32_t T_k, int32_t n_heads,
-                                   int32_t head_dim, int32_t with_importance);
+                                   int32_t head_dim, int32_t with_importance,
+                                   int32_t max_seqlen_q);
 
 /*
  * Bidirectional varlen attention over each sequence's whole paged cache, with
@@ -174,9 +178,10 @@ size_t fc_attention_workspace_size(int32_t B, int32_t T_q, int32_t T_k, int32_t 
  * out           [T_q, H, D]  dtype
  * importance    [H, T_k] fp32 or NULL
  * workspace     device memory of at least fc_attention_workspace_size() bytes
- *               (scratch for the longest-first sequence order; contents need no
- *               initialisation and are overwritten; calls that overlap on one
- *               workspace race)
+ *               (scratch for the longest-first sequence order, the key split's
+ *               partials and the column sums of row tiles past the first;
+ *               contents need no initialisation and are overwritten; calls that
+ *               overlap on one workspace race)
  * A sequence with L_b = 0 gets out = 0. Supported: bf16 with D = 128; f32 with
  * D in {64, 128}.
  */

@@ -71,6 +71,7 @@ struct AttnArgs {
   const int32_t* order;   // sequences, longest cache first (NULL = natural order)
   uint16_t* out;
   float* imp;
+  float* imp_part;        // row-tile split: column sums of row tiles 1.. [n_rt - 1][H][T_k]
   int maxp, log2ps, B, H, T_k, n_rt, accumulate;
   int lpt_inline;         // order == NULL and B <= 64: each workgroup ranks the sequences
   float scale_log2;  // softmax_scale * log2(e)
@@ -316,14 +317,24 @@ FC_DEVICE int reduced_key(int kb, int lane) { return s_key(kb, (lane >> 1) & 15,
 // so all four waves work when a sequence has 64 or fewer queries. The two waves of
 // a query half merge their row statistics after pass 1 and their O partials at the
 // end through LDS; importance sums the two waves that cover a key.
-template <bool WITH_IMP, bool PS_GE16, bool KS>
+//
+// RTS (row-tile split, importance path with more than 128 query rows in a
+// sequence): each row tile of a (sequence, head) gets its own workgroup, placed
+// like the one-pass path's, so the row tiles of an item stream its K/V through
+// one XCD's L2 together instead of one after another from memory. Row tile 0
+// writes (or adds) the importance; row tile r > 0 stores its column sums in
+// imp_part[r - 1], and attn_rowtile_reduce adds them in row-tile order.
+template <bool WITH_IMP, bool PS_GE16, bool KS, bool RTS = false>
 __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[A_LDS];
   float* red = (float*)(lds + 2 * A_STAGE);
+  // K/V loads: nontemporal where each block is read once per pass, the default
+  // policy where neighbouring workgroups read the same blocks at the same time
+  constexpr int POL = (WITH_IMP && !RTS) ? KV_POLICY : KV_POLICY_SHARED;
 
   int item = blockIdx.x;
   int rt_begin, rt_end;
-  if (WITH_IMP) {
+  if (WITH_IMP && !RTS) {
     rt_begin = 0;
     rt_end = a.n_rt;
   } else {
@@ -349,7 +360,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
   const float c = a.scale_log2;
 
   if (WITH_IMP && Q == 0 && !a.accumulate) {  // no query rows: column sums are 0
-    for (int key = t; key < L; key += blockDim.x) a.imp[(size_t)h * a.T_k + k0 + key] = 0.f;
+    if (rt_begin == 0)
+      for (int key = t; key < L; key += blockDim.x) a.imp[(size_t)h * a.T_k + k0 + key] = 0.f;
     return;
   }
   constexpr int ROWS = KS ? 64 : AROWS;        // query rows per row tile
@@ -372,12 +384,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
     if (WITH_IMP) {
       // ---------------- pass 1: row max and normaliser (K only) ----------------
       float m = -INFINITY, l = 0.f;
-      load_group<PS_GE16, false>(a, bt, h, 0, L, wave, lane, tr);
+      load_group<PS_GE16, false, POL>(a, bt, h, 0, L, wave, lane, tr);
       store_group<false>(lds, wave, lane, tr);
       __syncthreads();
       for (int tile = 0; tile < n_tiles; ++tile) {
         const bool more = tile + 1 < n_tiles;
-        load_group<PS_GE16, false>(a, bt, h, tile + 1, L, wave, lane, tr);
+        load_group<PS_GE16, false, POL>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
         f32x16_t s0 = s_block(ks, KS ? kbw : 0, qf, lane);
         f32x16_t s1;
@@ -434,11 +446,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
       const float off = row_ok ? mf + __builtin_amdgcn_logf(lf) : INFINITY;
 
       // ---------------- pass 2: P, O += P V, importance ----------------
-      load_group<PS_GE16, true>(a, bt, h, 0, L, wave, lane, tr);
+      load_group<PS_GE16, true, POL>(a, bt, h, 0, L, wave, lane, tr);
       store_group<true>(lds, wave, lane, tr);
       __syncthreads();
       for (int tile = 0; tile < n_tiles; ++tile) {
-        load_group<PS_GE16, true>(a, bt, h, tile + 1, L, wave, lane, tr);
+        load_group<PS_GE16, true, POL>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
         const char* vs = ks + K_TILE;
         float* rb = red + (tile & 1) * 4 * AKT;
@@ -463,8 +475,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
           if (key < L) {
             const float v = KS ? rb[(t >> 5) * 2 * AKT + t] + rb[((t >> 5) * 2 + 1) * AKT + t]
                                : rb[t] + rb[AKT + t] + rb[2 * AKT + t] + rb[3 * AKT + t];
-            float* dst = a.imp + (size_t)h * a.T_k + k0 + key;
-            *dst = (a.accumulate || rt > 0) ? *dst + v : v;
+            if (RTS && rt > 0) {
+              a.imp_part[((size_t)(rt - 1) * a.H + h) * a.T_k + k0 + key] = v;
+            } else {
+              float* dst = a.imp + (size_t)h * a.T_k + k0 + key;
+              *dst = (a.accumulate || rt > 0) ? *dst + v : v;
+            }
           }
         }
       }
@@ -584,6 +600,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
       __syncthreads();
     }
   }
+}
+
+// importance[h][j] += imp_part[0][h][j] + ... in row-tile order, for the keys of
+// sequences with more than one row tile: the same additions, in the same order,
+// as one workgroup walking the row tiles would make.
+__global__ __launch_bounds__(256) void attn_rowtile_reduce(AttnArgs a) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)a.H * a.T_k) return;
+  const int key = (int)(idx % a.T_k);
+  int lo = 0, hi = a.B;  // cu_k[lo] <= key < cu_k[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_k[mid] <= key) lo = mid; else hi = mid;
+  }
+  const int Q = a.cu_q[lo + 1] - a.cu_q[lo];
+  const int n_rt = (Q + AROWS - 1) / AROWS;
+  if (n_rt <= 1) return;
+  float acc = a.imp[idx];
+  for (int r = 1; r < n_rt; ++r) acc += a.imp_part[(size_t)(r - 1) * a.H * a.T_k + idx];
+  a.imp[idx] = acc;
 }
 
 // ---- key split for few (sequence, head) items (importance path) -------------
@@ -863,16 +899,34 @@ static int attn_key_splits(int B, int n_heads) {
   return n_cu / items < 8 ? (int)(n_cu / items) : 8;
 }
 
+// Extra importance levels of the row-tile split: sequences with more than one
+// 128-row tile (bf16 importance path; the key split only takes <= 128 rows).
+static int attn_rowtile_levels(int max_seqlen_q, int head_dim, int with_importance) {
+  if (!with_importance || head_dim != AD || max_seqlen_q <= AROWS) return 0;
+  return (int)(((int64_t)max_seqlen_q + AROWS - 1) / AROWS - 1);
+}
+
 extern "C" size_t fc_attention_workspace_size(int32_t B, int32_t T_q, int32_t T_k, int32_t n_heads,
-                                              int32_t head_dim, int32_t with_importance) {
-  (void)T_q; (void)T_k;
-  if (B <= 0) return 0;
+                                              int32_t head_dim, int32_t with_importance,
+                                              int32_t max_seqlen_q) {
+  (void)T_q;
+  if (B <= 0 || n_heads <= 0) return 0;
+  // products saturate at SIZE_MAX (a size no allocation can meet) instead of wrapping
+  auto mul = [](size_t x, size_t y) {
+    size_t r;
+    return __builtin_mul_overflow(x, y, &r) ? SIZE_MAX : r;
+  };
+  auto add = [](size_t x, size_t y) { return x > SIZE_MAX - y ? SIZE_MAX : x + y; };
   // the longest-first sequence order, then (key split) the chunk statistics
-  // and O partials
+  // and O partials, or (row-tile split) the column sums of row tiles 1..
   size_t bytes = (((size_t)B * sizeof(int32_t) + 255) / 256) * 256;
   const int S = (with_importance && head_dim == AD) ? attn_key_splits(B, n_heads) : 1;
-  if (S > 1)
-    bytes += (size_t)B * n_heads * S * AROWS * (sizeof(float2) + AD * sizeof(float));
+  if (S > 1 && max_seqlen_q <= AROWS)
+    bytes = add(bytes, mul(mul(mul((size_t)B, (size_t)n_heads), (size_t)S * AROWS),
+                           sizeof(float2) + AD * sizeof(float)));
+  const int lv = attn_rowtile_levels(max_seqlen_q, head_dim, with_importance);
+  if (lv > 0 && T_k > 0)
+    bytes = add(bytes, mul(mul(mul((size_t)lv, (size_t)n_heads), (size_t)T_k), sizeof(float)));
   return bytes;
 }
 
@@ -895,8 +949,10 @@ static fc_status_t attention_entry(
   FC_REQUIRE(softmax_scale > 0.f, FC_ERR_INVALID_VALUE,
              "fc_varlen_bidir_attention: softmax_scale must be > 0");
   FC_REQUIRE(workspace_bytes >= fc_attention_workspace_size(B, 0, T_k, n_heads, head_dim,
-                                                            importance != nullptr),
-             FC_ERR_WORKSPACE, "fc_varlen_bidir_attention: workspace too small");
+                                                            importance != nullptr, max_seqlen_q),
+             FC_ERR_WORKSPACE, "fc_varlen_bidir_attention: workspace too small (%zu < %zu bytes)",
+             workspace_bytes, fc_attention_workspace_size(B, 0, T_k, n_heads, head_dim,
+                                                          importance != nullptr, max_seqlen_q));
   FC_REQUIRE(workspace != nullptr, FC_ERR_WORKSPACE,
              "fc_varlen_bidir_attention: workspace required (fc_attention_workspace_size)");
   if (max_seqlen_q == 0) return FC_OK;
@@ -920,6 +976,7 @@ static fc_status_t attention_entry(
     a.order = (const int32_t*)workspace;
     a.out = (uint16_t*)out;
     a.imp = importance;
+    a.imp_part = nullptr;
     a.maxp = max_pages_per_seq;
     a.log2ps = log2ps;
     a.B = B;
@@ -927,7 +984,7 @@ static fc_status_t attention_entry(
     a.T_k = T_k;
     // every sequence fits one 64-row tile: split each tile's keys over the waves
     const bool ks = max_seqlen_q <= 64;
-    a.n_rt = ks ? 1 : (max_seqlen_q + AROWS - 1) / AROWS;
+    a.n_rt = ks ? 1 : (int)(((int64_t)max_seqlen_q + AROWS - 1) / AROWS);
     a.accumulate = accumulate ? 1 : 0;
     a.scale_log2 = softmax_scale * LOG2E;
     a.lpt_inline = B <= 64;
@@ -954,12 +1011,23 @@ static fc_status_t attention_entry(
       hipLaunchKernelGGL(attn_split_reduce, dim3(B * n_heads * AROWS), dim3(AD), 0, st, a, sp);
       return fc_check_launch("fc_varlen_bidir_attention");
     }
-    // one-pass: (sequence, head) items in groups of 8, one per XCD, each group's
-    // row tiles consecutive per XCD (see the kernel's block mapping)
-    const dim3 grid(importance ? B * n_heads : ((B * n_heads + 7) / 8) * 8 * a.n_rt);
+    // one-pass and row-tile split: (sequence, head) items in groups of 8, one
+    // per XCD, each group's row tiles consecutive per XCD (see the kernel's
+    // block mapping)
+    const bool rts = importance && !ks && a.n_rt > 1;
+    const dim3 grid(importance && !rts ? B * n_heads : ((B * n_heads + 7) / 8) * 8 * a.n_rt);
 #define FC_ATTN_LAUNCH(IMP, PS, KSP) \
     hipLaunchKernelGGL((attn_bf16_d128<IMP, PS, KSP>), grid, dim3(256), 0, st, a)
-    if (importance) {
+    if (rts) {
+      a.imp_part = (float*)((char*)workspace + (((size_t)B * sizeof(int32_t) + 255) / 256) * 256);
+      if (ps16)
+        hipLaunchKernelGGL((attn_bf16_d128<true, true, false, true>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_d128<true, false, false, true>), grid, dim3(256), 0, st, a);
+      const size_t n = (size_t)n_heads * T_k;
+      if (n > 0)
+        hipLaunchKernelGGL(attn_rowtile_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+    } else if (importance) {
       if (ps16) { if (ks) FC_ATTN_LAUNCH(true, true, true); else FC_ATTN_LAUNCH(true, true, false); }
       else { if (ks) FC_ATTN_LAUNCH(true, false, true); else FC_ATTN_LAUNCH(true, false, false); }
     } else {
@@ -1034,7 +1102,7 @@ extern "C" fc_status_t fc_varlen_bidir_attention_noalloc(
   FC_REQUIRE(B >= 1 && n_heads >= 1, FC_ERR_INVALID_VALUE,
              "fc_varlen_bidir_attention_noalloc: bad sizes B=%d n_heads=%d", B, n_heads);
   const size_t need = fc_attention_workspace_size(B, 0, T_k, n_heads, head_dim,
-                                                  importance != nullptr);
+                                                  importance != nullptr, max_seqlen_q);
   FC_REQUIRE(need <= FC_ATTN_SCRATCH_BYTES, FC_ERR_WORKSPACE,
              "fc_varlen_bidir_attention_noalloc: these sizes need %zu bytes of workspace, more "
              "than the %zu-byte static scratch (use fc_varlen_bidir_attention with a workspace)",

@@ -55,7 +55,7 @@ _SIGS = {
                                  P, P, SZ, I32, P], I32),
     "fc_rms_row_scale": ([P, I32, I32, F32, P, I32, P], I32),
     "fc_qkv_workspace_size": ([I32, I32, I32, I32], SZ),
-    "fc_attention_workspace_size": ([I32, I32, I32, I32, I32, I32], SZ),
+    "fc_attention_workspace_size": ([I32, I32, I32, I32, I32, I32, I32], SZ),
     "fc_varlen_bidir_attention": ([P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, F32, P, P,
                                    I32, P, SZ, I32, P], I32),
     "fc_importance_topk": ([P, P, I32, I32, I32, P, I32, P, P, P, P], I32),
@@ -142,9 +142,10 @@ def fc_rms_row_scale(x, M, N, eps, scale, dtype, stream=None):
     _check("fc_rms_row_scale", st)
 
 
-def fc_attention_workspace_size(B, T_q, T_k, n_heads, head_dim, with_importance) -> int:
+def fc_attention_workspace_size(B, T_q, T_k, n_heads, head_dim, with_importance,
+                                max_seqlen_q) -> int:
     return int(load().fc_attention_workspace_size(B, T_q, T_k, n_heads, head_dim,
-                                                  int(bool(with_importance))))
+                                                  int(bool(with_importance)), max_seqlen_q))
 
 
 def fc_varlen_bidir_attention(q, k_cache, v_cache, block_table, max_pages_per_seq, page_size,

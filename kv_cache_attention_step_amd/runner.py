@@ -91,7 +91,8 @@ class StepBuffers:
         self.topk_pos = torch.empty((self.B, k), dtype=torch.int32, device=device)
         self.topk_count = torch.empty(self.B, dtype=torch.int32, device=device)
         self.topk_score = torch.empty((self.B, k), dtype=torch.float32, device=device)
-        ws = fc.fc_attention_workspace_size(self.B, self.T_q, self.T_k, self.H, self.D, 1)
+        ws = fc.fc_attention_workspace_size(self.B, self.T_q, self.T_k, self.H, self.D, 1,
+                                            int(inp.max_seqlen_q))
         self.ws_bytes = ws
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws else None
         qws = fc.fc_qkv_workspace_size(self.T_q, self.H * self.D, self.D, self.dtype)
@@ -259,7 +260,8 @@ class LayerStackDriver:
         self.topk_pos = torch.full((self.B, self.k), -1, dtype=torch.int32, device=device)
         self.topk_count = torch.zeros(self.B, dtype=torch.int32, device=device)
         self.topk_score = torch.empty((self.B, self.k), dtype=torch.float32, device=device)
-        ws = fc.fc_attention_workspace_size(self.B, T_max, self.T_k, self.H, self.D, 1)
+        ws = fc.fc_attention_workspace_size(self.B, T_max, self.T_k, self.H, self.D, 1,
+                                            max(x["Q"] for x in self.steps))
         self.ws_bytes = ws
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
         qws = fc.fc_qkv_workspace_size(T_max, self.H * self.D, self.D, self.dtype)
@@ -357,7 +359,7 @@ class TwoViewVerifyBuffers:
         qws = fc.fc_qkv_workspace_size(self.T_q, self.d, D, self.dtype)
         self.qkv_ws_bytes = qws
         self.qkv_workspace = torch.empty(max(qws, 1), dtype=torch.uint8, device=device)
-        ws = fc.fc_attention_workspace_size(2 * B, self.T_q, self.T_kv, H, D, 0)
+        ws = fc.fc_attention_workspace_size(2 * B, self.T_q, self.T_kv, H, D, 0, self.max_q)
         self.ws_bytes = ws
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
         self.accept_pos = torch.zeros(self.n_pos, dtype=torch.uint8, device=device)

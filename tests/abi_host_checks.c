@@ -73,8 +73,13 @@ int main(void) {
     size_t c = fc_qkv_workspace_size(0x7fffffff, 256, 128, FC_DTYPE_BF16);
     if (!(a > 0 && b >= a && c >= b / 16)) { fprintf(stderr, "FAIL qkv workspace sizes\n"); ++failures; }
     if (fc_qkv_workspace_size(-5, 4096, 128, FC_DTYPE_BF16) != 0) { fprintf(stderr, "FAIL ws<0\n"); ++failures; }
-    size_t w = fc_attention_workspace_size(0x7fffffff, 0x7fffffff, 0x7fffffff, 1 << 20, 128, 1);
+    size_t w = fc_attention_workspace_size(0x7fffffff, 0x7fffffff, 0x7fffffff, 1 << 20, 128, 1, 64);
     if (w == 0) { fprintf(stderr, "FAIL attention workspace\n"); ++failures; }
+    /* a request too large for any allocation saturates instead of wrapping */
+    size_t w2 = fc_attention_workspace_size(4, 0x7fffffff, 0x7fffffff, 0x7fffffff, 128, 1, 0x7fffffff);
+    if (w2 != (size_t)-1) { fprintf(stderr, "FAIL attention workspace saturation\n"); ++failures; }
+    size_t w3 = fc_attention_workspace_size(4, 1024, 1000, 8, 128, 1, 300);   /* 2 extra row tiles */
+    if (w3 < (size_t)2 * 8 * 1000 * 4) { fprintf(stderr, "FAIL attention row-tile workspace\n"); ++failures; }
   }
 
   /* attention */

@@ -118,7 +118,7 @@ def test_attention_argument_checks():
     expect("FC_ERR_INVALID_VALUE", softmax_scale=0.0)
     expect("FC_ERR_INVALID_VALUE", dtype=3)
     expect("FC_ERR_UNSUPPORTED", head_dim=64)
-    need = fc.fc_attention_workspace_size(2, 8, 64, 2, 128, 1)
+    need = fc.fc_attention_workspace_size(2, 8, 64, 2, 128, 1, 8)
     assert need >= 2 * 4
     expect("FC_ERR_WORKSPACE", workspace_bytes=need - 1)
     expect("FC_ERR_WORKSPACE", workspace=None)

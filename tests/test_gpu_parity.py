@@ -445,7 +445,7 @@ def _attention_direct(torch, q_bits, k_cache, v_cache, table, page_size, cu_q, c
     bt, cq, ck = t(table), t(cu_q), t(cu_k)
     out = torch.empty((T_q, H, D), dtype=torch.int16, device=dev)
     imp = torch.full((H, T_k), float("nan"), dtype=torch.float32, device=dev) if with_importance else None
-    wsb = fc.fc_attention_workspace_size(B, T_q, T_k, H, D, with_importance)
+    wsb = fc.fc_attention_workspace_size(B, T_q, T_k, H, D, with_importance, max_seqlen_q)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     fc.fc_varlen_bidir_attention(q, kc, vc, bt, table.shape[1], page_size, cq, ck, B, max_seqlen_q,
                                  T_k, H, D, 1.0 / math.sqrt(D), out, imp, 0, ws, wsb, fc.FC_DTYPE_BF16)

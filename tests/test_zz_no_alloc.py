@@ -55,7 +55,7 @@ def _run(torch, c, with_imp, noalloc):
     if noalloc:
         fc.fc_varlen_bidir_attention_noalloc(*args, fc.FC_DTYPE_BF16)
     else:
-        wsb = fc.fc_attention_workspace_size(B, T_q, T_k, H, 128, with_imp)
+        wsb = fc.fc_attention_workspace_size(B, T_q, T_k, H, 128, with_imp, int(c["Q"].max()))
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
         fc.fc_varlen_bidir_attention(*args, ws, wsb, fc.FC_DTYPE_BF16)
     torch.cuda.synchronize()
@@ -94,7 +94,7 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     from kv_cache_attention_step_amd import flashcache as fc
     fc.load()
     B = 8_000_000            # the longest-first order alone needs 32 MB
-    assert fc.fc_attention_workspace_size(B, 0, 0, 32, 128, 1) > fc.FC_ATTN_NOALLOC_SCRATCH_BYTES
+    assert fc.fc_attention_workspace_size(B, 0, 0, 32, 128, 1, 128) > fc.FC_ATTN_NOALLOC_SCRATCH_BYTES
     fake = 0x1000
     with pytest.raises(fc.FlashCacheError) as ei:
         fc.fc_varlen_bidir_attention_noalloc(fake, fake, fake, fake, 4, 16, fake, fake, B, 128,
