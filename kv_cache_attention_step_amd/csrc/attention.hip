@@ -60,6 +60,7 @@ constexpr int KV_POLICY = 2;
 // view-private page table shares the prefix), and the nontemporal policy
 // evicts them from L2 before that read.
 constexpr int KV_POLICY_SHARED = 0;
+constexpr bool ONEPASS_MIXED = true;   // short last row tiles use the key-split layout
 
 struct AttnArgs {
   const uint16_t* q;
@@ -324,7 +325,10 @@ FC_DEVICE int reduced_key(int kb, int lane) { return s_key(kb, (lane >> 1) & 15,
 // one XCD's L2 together instead of one after another from memory. Row tile 0
 // writes (or adds) the importance; row tile r > 0 stores its column sums in
 // imp_part[r - 1], and attn_rowtile_reduce adds them in row-tile order.
-template <bool WITH_IMP, bool PS_GE16, bool KS, bool RTS = false>
+//
+// MIXED (one-pass path, 128-row tiles): a row tile with at most 64 rows left
+// (the last tile of a sequence) takes the KS layout, so all four waves work on it.
+template <bool WITH_IMP, bool PS_GE16, bool KS, bool RTS = false, bool MIXED = false>
 __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[A_LDS];
   float* red = (float*)(lds + 2 * A_STAGE);
@@ -365,10 +369,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
     return;
   }
   constexpr int ROWS = KS ? 64 : AROWS;        // query rows per row tile
-  const int qh = KS ? (wave & 1) : wave;        // 32-row group of this wave
-  const int kbw = KS ? (wave >> 1) : 0;         // its key block (KS)
   for (int rt = rt_begin; rt < rt_end; ++rt) {
     if (rt * ROWS >= Q) break;
+    const bool kst = MIXED ? (Q - rt * ROWS <= 64) : KS;   // key-split layout for this tile
+    const int qh = kst ? (wave & 1) : wave;       // 32-row group of this wave
+    const int kbw = kst ? (wave >> 1) : 0;        // its key block (key-split layout)
     const int row = rt * ROWS + qh * 32 + (lane & 31);
     const bool row_ok = row < Q;
     if (L == 0) {  // no keys: output 0
@@ -515,26 +520,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         load_group<PS_GE16, true, KV_POLICY_SHARED>(a, bt, h, tile + 1, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
         const char* vs = ks + K_TILE;
-        const int kb0 = KS ? kbw : 0;
+        const int kb0 = kst ? kbw : 0;
         f32x16_t s0 = s_block(ks, kb0, qf, lane);
         f32x16_t s1;
-        if (!KS) s1 = s_block(ks, 1, qf, lane);
+        if (!kst) s1 = s_block(ks, 1, qf, lane);
         if (ragged && !more) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             if (tile * AKT + s_key(kb0, i, lane) >= L) s0[i] = -INFINITY;
-            if (!KS && tile * AKT + s_key(1, i, lane) >= L) s1[i] = -INFINITY;
+            if (!kst && tile * AKT + s_key(1, i, lane) >= L) s1[i] = -INFINITY;
           }
         }
         float tmax = s0[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s0[i]);
-        if (!KS) {
+        if (!kst) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
-        // without KS key 0 of the first tile is valid, so mn is finite; with KS a key
+        // without the key split key 0 of the first tile is valid, so mn is finite; with it a key
         // block can be empty (L <= 32): then mn stays -inf and P = 0
         const float mn = fmaxf(m, tmax);
         const float mref = mn == -INFINITY ? 0.f : mn;
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
           s0[i] = fexp2(fmaf(s0[i], c, -mref));
           sum += s0[i];
         }
-        if (!KS) {
+        if (!kst) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             s1[i] = fexp2(fmaf(s1[i], c, -mref));
@@ -562,7 +567,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         }
         pv_chunk(vs, kb0, 0, s0, o, lane);
         pv_chunk(vs, kb0, 1, s0, o, lane);
-        if (!KS) {
+        if (!kst) {
           pv_chunk(vs, 1, 0, s1, o, lane);
           pv_chunk(vs, 1, 1, s1, o, lane);
         }
@@ -570,7 +575,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         __syncthreads();
       }
       float lt = l + __shfl_xor(l, 32);
-      if (KS) {  // merge (m, l, O) with the wave of the other key block (split-max merge)
+      if (kst) {  // merge (m, l, O) with the wave of the other key block (split-max merge)
         float* xo = (float*)lds;   // [2][64 x 64] O partials, then [2][64] (m, l)
         float* xs = xo + 2 * 4096;
         if (kbw == 1) {
@@ -1031,8 +1036,13 @@ static fc_status_t attention_entry(
       if (ps16) { if (ks) FC_ATTN_LAUNCH(true, true, true); else FC_ATTN_LAUNCH(true, true, false); }
       else { if (ks) FC_ATTN_LAUNCH(true, false, true); else FC_ATTN_LAUNCH(true, false, false); }
     } else {
-      if (ps16) { if (ks) FC_ATTN_LAUNCH(false, true, true); else FC_ATTN_LAUNCH(false, true, false); }
-      else { if (ks) FC_ATTN_LAUNCH(false, false, true); else FC_ATTN_LAUNCH(false, false, false); }
+      // one-pass: with more than 64 rows somewhere, 128-row tiles whose short last
+      // tiles take the key-split layout
+#define FC_ATTN_LAUNCH_MIXED(PS) \
+      hipLaunchKernelGGL((attn_bf16_d128<false, PS, false, false, ONEPASS_MIXED>), grid, dim3(256), 0, st, a)
+      if (ps16) { if (ks) FC_ATTN_LAUNCH(false, true, true); else FC_ATTN_LAUNCH_MIXED(true); }
+      else { if (ks) FC_ATTN_LAUNCH(false, false, true); else FC_ATTN_LAUNCH_MIXED(false); }
+#undef FC_ATTN_LAUNCH_MIXED
     }
 #undef FC_ATTN_LAUNCH
     return fc_check_launch("fc_varlen_bidir_attention");

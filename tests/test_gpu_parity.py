@@ -484,6 +484,76 @@ def test_attention_short_query_tiles(torch_cuda):
             PU.assert_importance_close(imp, ref_imp)
 
 
+@pytest.mark.parametrize("ps", [16, 4])
+@pytest.mark.parametrize("accumulate", [0, 1])
+def test_attention_long_queries_row_tile_split(torch_cuda, ps, accumulate):
+    """Sequences of 0, 100, 129, 300 and 513 query rows (one to five 128-row tiles):
+    with importance, every row tile beyond the first runs in its own workgroup and
+    its column sums are added to row tile 0's in row-tile order. Attention out and
+    importance against the oracle, with importance written (accumulate 0) and added
+    to a prefilled buffer (accumulate 1: the zero-row sequence keeps its prefill);
+    then the one-pass path on the same inputs (short last tiles in the key-split
+    layout)."""
+    torch = torch_cuda
+    from kv_cache_attention_step_amd import flashcache as fc
+    _say(f"case long queries, row-tile split (page size {ps}, accumulate {accumulate})")
+    cfg = dataclasses.replace(SMALL_BF16, name="long-q", seed=31, page_size=ps)
+    H, D = cfg.n_heads, cfg.head_dim
+    rng = W.rng_for(31, ps)
+    L = np.array([300, 64, 777, 1500, 900], np.int64)
+    Q = np.array([0, 100, 129, 300, 513], np.int64)
+    cfg = dataclasses.replace(cfg, batch=len(L))
+    table, num_pages = W.draw_paging(cfg, L, rng)
+    k_cache, v_cache = W.draw_cache(cfg, num_pages, rng, cache_len=L, block_table=table,
+                                    tail_nan=True)
+    cu_q = np.concatenate([[0], np.cumsum(Q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    T_q, T_k = int(cu_q[-1]), int(cu_k[-1])
+    q_bits = W.to_bf16_bits(rng.standard_normal((T_q, H, D), dtype=np.float32) * 1.3)
+    ref_o, ref_imp = O.varlen_attention(O.bf16_to_f64(q_bits), O.bf16_to_f64(k_cache),
+                                        O.bf16_to_f64(v_cache), table, ps, cu_q, cu_k,
+                                        1.0 / math.sqrt(D))
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    prefill = np.float32(0.25)
+    imp = torch.full((H, T_k), float(prefill) if accumulate else float("nan"),
+                     dtype=torch.float32, device=dev)
+    out = torch.empty((T_q, H, D), dtype=torch.int16, device=dev)
+    wsb = fc.fc_attention_workspace_size(len(L), T_q, T_k, H, D, 1, int(Q.max()))
+    assert wsb >= 4 * H * T_k * 4      # four levels of column sums past row tile 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    fc.fc_varlen_bidir_attention(t(q_bits.view(np.int16)), t(k_cache.view(np.int16)),
+                                 t(v_cache.view(np.int16)), t(table), table.shape[1], ps, t(cu_q),
+                                 t(cu_k), len(L), int(Q.max()), T_k, H, D, 1.0 / math.sqrt(D), out,
+                                 imp, accumulate, ws, wsb, fc.FC_DTYPE_BF16)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint16)
+    got = imp.cpu().numpy().astype(np.float64)
+    PU.assert_close(O.bf16_to_f64(o), ref_o, "bf16", "attention out")
+    if accumulate:
+        z = slice(int(cu_k[0]), int(cu_k[1]))
+        assert np.all(got[:, z] == prefill), "a sequence without query rows kept its prefill"
+        got = got - float(prefill)
+    PU.assert_importance_close(got, ref_imp)
+    # per head, a sequence's column sums add up to its query rows
+    for b in range(1, len(L)):
+        sums = got[:, cu_k[b]:cu_k[b + 1]].sum(axis=1)
+        np.testing.assert_allclose(sums, Q[b], rtol=2e-4)
+    if accumulate == 0:
+        # the one-pass path on the same inputs: 128-row tiles, the last tile of 129,
+        # 300 and 513 rows (1, 44 and 1 rows left) in the key-split layout
+        wsb1 = fc.fc_attention_workspace_size(len(L), T_q, T_k, H, D, 0, int(Q.max()))
+        ws1 = torch.empty(max(wsb1, 1), dtype=torch.uint8, device=dev)
+        out1 = torch.empty((T_q, H, D), dtype=torch.int16, device=dev)
+        fc.fc_varlen_bidir_attention(t(q_bits.view(np.int16)), t(k_cache.view(np.int16)),
+                                     t(v_cache.view(np.int16)), t(table), table.shape[1], ps,
+                                     t(cu_q), t(cu_k), len(L), int(Q.max()), T_k, H, D,
+                                     1.0 / math.sqrt(D), out1, None, 0, ws1, wsb1, fc.FC_DTYPE_BF16)
+        torch.cuda.synchronize()
+        PU.assert_close(O.bf16_to_f64(out1.cpu().numpy().view(np.uint16)), ref_o, "bf16",
+                        "one-pass attention out")
+
+
 def test_verify_small_vocab(torch_cuda):
     torch = torch_cuda
     from kv_cache_attention_step_amd.runner import VerifyBuffers
