@@ -226,9 +226,11 @@ fc_status_t fc_varlen_bidir_attention_noalloc(
  * candidate_mask  [T_k] uint8 or NULL
  * topk_pos        [B, k] chosen positions (within the sequence) in ascending
  *                 order, -1 after the last one
- * topk_count      [B] number chosen; -1 if L_b exceeds FC_TOPK_MAX_LEN (that
- *                 sequence's row is then left as all -1)
+ * topk_count      [B] number chosen: min(k, candidates of the sequence)
  * topk_score      [B, k] fp32 scores in the same order (NaN padded) or NULL
+ * Sequences of up to FC_TOPK_MAX_LEN keys keep their scores in LDS; longer ones
+ * are served too, recomputing the head sums from `importance` in each of the
+ * selection's passes (the same sums, several times the reads).
  */
 #define FC_TOPK_MAX_LEN 16384
 fc_status_t fc_importance_topk(

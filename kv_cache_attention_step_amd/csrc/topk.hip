@@ -4,7 +4,8 @@
 // Tracked positions are the top-k decoded tokens by attention importance
 // (signal-papers page on arXiv 2609.26796, Fig. 2). One workgroup per sequence:
 //   1. score_j = sum over heads (ascending head order, fp32) of importance[h, j],
-//      kept in LDS with the candidate flag;
+//      kept in LDS with the candidate flag (sequences longer than the LDS
+//      holds recompute them from global memory in every pass instead);
 //   2. exact radix select (4 passes of 8 bits over an order-preserving uint32
 //      image of the score, LDS histograms with integer atomics) finds the k-th
 //      largest score T and how many entries equal to T are still needed;
@@ -58,37 +59,43 @@ FC_DEVICE int block_exclusive_scan(int v, int* buf, int* out_excl) {
   return total;
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(
-    const float* __restrict__ imp, const int32_t* __restrict__ cu_k, int T_k, int H,
-    const uint8_t* __restrict__ cand_mask, int k, int32_t* __restrict__ topk_pos,
-    int32_t* __restrict__ topk_count, float* __restrict__ topk_score) {
-  __shared__ float s_score[FC_TOPK_MAX_LEN];
-  __shared__ uint8_t s_cand[FC_TOPK_MAX_LEN];
-  __shared__ int s_hist[256];
-  __shared__ int s_scan[TK_WAVES + 1];
-  __shared__ int s_ctl[4];
+// Head-summed score of key j of a sequence whose keys start at k0: heads added
+// in ascending order (the order the LDS path uses, so both give the same bits).
+FC_DEVICE float head_sum_at(const float* __restrict__ imp, size_t k0j, int T_k, int H) {
+  float s = 0.f;
+  for (int h = 0; h < H; ++h) s += imp[(size_t)h * T_k + k0j];
+  return s;
+}
 
-  const int b = blockIdx.x;
+// The selection for one sequence. LDS (L <= FC_TOPK_MAX_LEN): scores and
+// candidate flags are computed once into LDS. STREAM (longer sequences): every
+// pass recomputes them from global memory (the same additions in the same
+// order), so any length is served, at several times the reads.
+template <bool STREAM>
+FC_DEVICE void topk_select_seq(const float* __restrict__ imp, int T_k, int H,
+                               const uint8_t* __restrict__ cand_mask, int k, int k0, int L,
+                               int32_t* __restrict__ out_pos, float* __restrict__ out_sc,
+                               int32_t* __restrict__ count_out, float* s_score, uint8_t* s_cand,
+                               int* s_hist, int* s_scan, int* s_ctl) {
   const int t = threadIdx.x;
-  const int k0 = cu_k[b];
-  const int L = cu_k[b + 1] - k0;
-  int32_t* out_pos = topk_pos + (size_t)b * k;
-  float* out_sc = topk_score ? topk_score + (size_t)b * k : nullptr;
-
-  if (L > FC_TOPK_MAX_LEN) {
-    for (int i = t; i < k; i += TK_THREADS) {
-      out_pos[i] = -1;
-      if (out_sc) out_sc[i] = NAN;
-    }
-    if (t == 0) topk_count[b] = -1;
-    return;
-  }
+  auto score_of = [&](int j) -> float {
+    if (STREAM) return head_sum_at(imp, (size_t)k0 + j, T_k, H);
+    return s_score[j];
+  };
+  auto cand_of = [&](int j) -> bool {
+    if (STREAM) return cand_mask ? cand_mask[k0 + j] != 0 : true;
+    return s_cand[j] != 0;
+  };
 
   // 1. head-summed scores (heads added in ascending order) and candidate flags;
   //    up to 32 loads are issued before their additions (one memory latency per
   //    key for up to 32 heads)
   int my_cand = 0;
   for (int j = t; j < L; j += TK_THREADS) {
+    if (STREAM) {
+      my_cand += cand_of(j);
+      continue;
+    }
     const float* src = imp + k0 + j;
     float s = 0.f;
     int h = 0;
@@ -124,8 +131,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
       if (t < 256) s_hist[t] = 0;
       __syncthreads();
       for (int j = t; j < L; j += TK_THREADS) {
-        if (!s_cand[j]) continue;
-        const uint32_t key = order_key(s_score[j]);
+        if (!cand_of(j)) continue;
+        const uint32_t key = order_key(score_of(j));
         if ((key & prefix_mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1);
       }
       __syncthreads();
@@ -171,15 +178,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
   const int j0 = min(L, t * per), j1 = min(L, j0 + per);
   int n_eq = 0;
   for (int j = j0; j < j1; ++j)
-    if (kk > 0 && s_cand[j] && order_key(s_score[j]) == T) ++n_eq;
+    if (kk > 0 && cand_of(j) && order_key(score_of(j)) == T) ++n_eq;
   int eq_before;
   block_exclusive_scan(n_eq, s_scan, &eq_before);
   int n_sel = 0;
   {
     int e = eq_before;
     for (int j = j0; j < j1; ++j) {
-      if (kk == 0 || !s_cand[j]) continue;
-      const uint32_t key = order_key(s_score[j]);
+      if (kk == 0 || !cand_of(j)) continue;
+      const uint32_t key = order_key(score_of(j));
       if (key > T) ++n_sel;
       else if (key == T) { if (e < need) ++n_sel; ++e; }
     }
@@ -189,14 +196,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
   {
     int e = eq_before, r = sel_before;
     for (int j = j0; j < j1; ++j) {
-      if (kk == 0 || !s_cand[j]) continue;
-      const uint32_t key = order_key(s_score[j]);
+      if (kk == 0 || !cand_of(j)) continue;
+      const float sc = score_of(j);
+      const uint32_t key = order_key(sc);
       bool take = false;
       if (key > T) take = true;
       else if (key == T) { take = e < need; ++e; }
       if (take) {
         out_pos[r] = j;
-        if (out_sc) out_sc[r] = s_score[j];
+        if (out_sc) out_sc[r] = sc;
         ++r;
       }
     }
@@ -205,7 +213,30 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     out_pos[i] = -1;
     if (out_sc) out_sc[i] = NAN;
   }
-  if (t == 0) topk_count[b] = kk;
+  if (t == 0) *count_out = kk;
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(
+    const float* __restrict__ imp, const int32_t* __restrict__ cu_k, int T_k, int H,
+    const uint8_t* __restrict__ cand_mask, int k, int32_t* __restrict__ topk_pos,
+    int32_t* __restrict__ topk_count, float* __restrict__ topk_score) {
+  __shared__ float s_score[FC_TOPK_MAX_LEN];
+  __shared__ uint8_t s_cand[FC_TOPK_MAX_LEN];
+  __shared__ int s_hist[256];
+  __shared__ int s_scan[TK_WAVES + 1];
+  __shared__ int s_ctl[4];
+
+  const int b = blockIdx.x;
+  const int k0 = cu_k[b];
+  const int L = cu_k[b + 1] - k0;
+  int32_t* out_pos = topk_pos + (size_t)b * k;
+  float* out_sc = topk_score ? topk_score + (size_t)b * k : nullptr;
+  if (L > FC_TOPK_MAX_LEN)
+    topk_select_seq<true>(imp, T_k, H, cand_mask, k, k0, L, out_pos, out_sc, topk_count + b,
+                          s_score, s_cand, s_hist, s_scan, s_ctl);
+  else
+    topk_select_seq<false>(imp, T_k, H, cand_mask, k, k0, L, out_pos, out_sc, topk_count + b,
+                           s_score, s_cand, s_hist, s_scan, s_ctl);
 }
 
 __global__ void assemble_kernel(const int32_t* __restrict__ topk_pos,
