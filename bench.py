@@ -49,6 +49,8 @@ def parse():
                     help="sequences of the batch the CPU oracle baseline runs")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0,
                     help="seconds of CPU work for each oracle baseline leg (all threads, 1 thread)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the timing of the step captured as a HIP graph")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured-peak probes (MFMA rate, KV-cache streaming rate)")
     ap.add_argument("--sweep", choices=("batch", "query"), default=None,
@@ -637,6 +639,32 @@ def main():
     for i in range(args.steps):
         one_step(evs[i], split=True)
     torch.cuda.synchronize()
+    # the same step captured once as a HIP graph and replayed: the kernels are the
+    # same, the host enqueues one graph instead of five launches
+    graph_ms = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            bufs.assemble(stream)
+            bufs.qkv(stream)
+            bufs.attention(stream)
+            bufs.topk(stream)
+        torch.cuda.synchronize()
+        gts = []
+        for i in range(args.warmup + args.steps):
+            if flush is not None:
+                with torch.cuda.stream(stream):
+                    flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            with torch.cuda.stream(stream):
+                graph.replay()
+            e1.record(stream)
+            if i >= args.warmup:
+                gts.append((e0, e1))
+        torch.cuda.synchronize()
+        graph_ms = round(float(np.median([a.elapsed_time(b) for a, b in gts])), 4)
+        del graph
     seg = lambda a, b, e_=None: np.array([e[a].elapsed_time(e[b]) for e in (e_ or evs)]) * 1e3  # us
     k0, k1, k2, k3 = seg(0, 1), seg(1, 2), seg(2, 3), seg(3, 4)
     step_ms = seg(0, 4, evs_step) * 1e-3
@@ -725,7 +753,8 @@ def main():
                                 "step boundaries only; kernel entries (mean and median) from "
                                 "a second run of as many steps with events between kernels",
                    "ms_per_step_mean": round(float(step_ms.mean()), 4),
-                   "ms_per_step_with_kernel_events": round(float(np.median(seg(0, 4))) * 1e-3, 4)},
+                   "ms_per_step_with_kernel_events": round(float(np.median(seg(0, 4))) * 1e-3, 4),
+                   "ms_per_step_graph_replay": graph_ms},
         "verify_accept_c4": verify,
         "verify_attention_c4": verify_attn,
         "verify_two_views_c4": verify_views,
