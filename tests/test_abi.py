@@ -165,6 +165,34 @@ def test_last_error_message_names_the_call():
     assert b"fc_importance_topk" in lib.fc_last_error()
 
 
+def test_last_error_is_per_thread():
+    """Two host threads each make a rejected call, then (after both have) read the
+    message: each sees its own call's message, not the other thread's."""
+    import threading
+    lib = _lib()
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def topk_thread():
+        st = lib.fc_importance_topk(None, None, 0, 0, 0, None, 0, None, None, None, None)
+        barrier.wait()
+        seen["topk"] = (st, lib.fc_last_error())
+
+    def linear_thread():
+        st = lib.fc_linear_residual(None, None, None, 0, 0, 0, 0, None)
+        barrier.wait()
+        seen["linear"] = (st, lib.fc_last_error())
+
+    threads = [threading.Thread(target=topk_thread), threading.Thread(target=linear_thread)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=30)
+    assert seen["topk"][0] != 0 and b"fc_importance_topk" in seen["topk"][1]
+    assert seen["linear"][0] != 0 and b"fc_linear_residual" in seen["linear"][1]
+    assert b"fc_linear_residual" not in seen["topk"][1]
+
+
 def _sanitized_build(tmp):
     """Library sources with AddressSanitizer and UndefinedBehaviorSanitizer on
     their host code (device code unchanged), linked with the C harness into one
