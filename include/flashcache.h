@@ -299,8 +299,10 @@ fc_status_t fv_lmhead_verify_accept(const void* hidden, const void* w_lm, int32_
  *   conf[r]   = 1 / sum_v exp(logits[r, v] - logits[r, argmax[r]])   (fp32)
  *   accept[r] = conf[r] >= tau   (fp32, inclusive)
  * With at_least_one != 0, a sequence none of whose rows passed accepts its
- * row of largest conf (equal conf: the lower row), so each step unmasks at
- * least one token per sequence.
+ * row of largest conf (equal conf: the lower row; NaN conf, from non-finite
+ * logits, never counts as largest, and a sequence whose rows are all NaN
+ * accepts its first row), so each step unmasks at least one token per
+ * sequence.
  * logits [R, vocab] bf16, R = cu_positions[B]; argmax [R] int32, conf [R]
  * fp32, accept [R] uint8.
  */

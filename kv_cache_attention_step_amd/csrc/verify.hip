@@ -232,6 +232,8 @@ __global__ __launch_bounds__(64) void accept_at_least_one(const float* __restric
       best_p = op;
     }
   }
+  // no comparable confidence at all (every row NaN): the sequence's first row
+  if (best_p >= p1) best_p = p0;
   if (lane == 0 && !any) accept[best_p] = 1;
 }
 
