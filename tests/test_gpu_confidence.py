@@ -95,3 +95,24 @@ def test_confidence_mask_view_full_vocab(torch_cuda):
                 if len(top) < 2 or top[0] - top[1] > 1e-5 * top[0]:
                     assert np.array_equal(seg_g, seg_o), f"sequence {b}: fallback row"
     assert acc0.sum() > 0 and acc1.sum() > acc0.sum()   # both rules exercised
+
+
+def test_confidence_at_least_one_with_non_finite_rows(torch_cuda):
+    """A sequence whose logits are all NaN next to ordinary sequences: with the
+    at-least-one rule it still gets exactly one accepted row when none passed,
+    inside its own rows, and the other sequences are unaffected."""
+    _say("case confidence acceptance: a sequence of NaN rows")
+    rng = np.random.default_rng(5)
+    V = 512
+    cu = np.array([0, 4, 9, 12], np.int32)
+    rows = (rng.standard_normal((int(cu[-1]), V)) * 2).astype(np.float32)
+    rows[4:9] = np.nan                       # sequence 1: every logit NaN
+    bits = W.to_bf16_bits(rows)
+    am, cf, ac = _run(torch_cuda, bits, cu, 0.9, 1)
+    assert set(np.unique(ac)) <= {0, 1}
+    assert ac[4:9].sum() >= 1, "the NaN sequence accepts at least one row"
+    ok = np.r_[0:4, 9:12]
+    am_r, cf_r, acc_r = O.confidence_accept(bits[ok], np.array([0, 4, 7], np.int32), 0.9, True)
+    assert np.array_equal(am[ok], am_r)
+    np.testing.assert_allclose(cf[ok], cf_r, rtol=2e-6)
+    assert np.array_equal(ac[ok], acc_r)
