@@ -173,39 +173,48 @@ FC_DEVICE void topk_select_seq(const float* __restrict__ imp, int T_k, int H,
   }
   const uint32_t T = prefix;  // exact key of the kk-th largest; `need` entries equal to T are taken
 
-  // 3. chosen flags in position order: contiguous chunk per thread
-  const int per = (L + TK_THREADS - 1) / TK_THREADS;
+  // 3. output in position order: a contiguous chunk per thread; one scan of the
+  //    packed counts (keys above T) << 16 | (keys equal to T) gives each chunk
+  //    the counts before it, and an entry's output index is the keys above T
+  //    before it plus min(keys equal to T before it, need)
+  const int per = (L + TK_THREADS - 1) / TK_THREADS;   // keys per thread
   const int j0 = min(L, t * per), j1 = min(L, j0 + per);
-  int n_eq = 0;
-  for (int j = j0; j < j1; ++j)
-    if (kk > 0 && cand_of(j) && order_key(score_of(j)) == T) ++n_eq;
-  int eq_before;
-  block_exclusive_scan(n_eq, s_scan, &eq_before);
-  int n_sel = 0;
-  {
-    int e = eq_before;
+  int n_gt = 0, n_eq = 0;
+  if (kk > 0) {
     for (int j = j0; j < j1; ++j) {
-      if (kk == 0 || !cand_of(j)) continue;
+      if (!cand_of(j)) continue;
       const uint32_t key = order_key(score_of(j));
-      if (key > T) ++n_sel;
-      else if (key == T) { if (e < need) ++n_sel; ++e; }
+      n_gt += key > T;
+      n_eq += key == T;
     }
   }
-  int sel_before;
-  block_exclusive_scan(n_sel, s_scan, &sel_before);
-  {
-    int e = eq_before, r = sel_before;
+  int gt_before, eq_before;
+  if (L <= 32767) {
+    int packed;
+    block_exclusive_scan((n_gt << 16) | n_eq, s_scan, &packed);
+    gt_before = packed >> 16;
+    eq_before = packed & 0xFFFF;
+  } else {  // counts beyond 16 bits (streamed sequences): two scans
+    block_exclusive_scan(n_gt, s_scan, &gt_before);
+    block_exclusive_scan(n_eq, s_scan, &eq_before);
+  }
+  if (kk > 0) {
+    int g = gt_before, e = eq_before;
     for (int j = j0; j < j1; ++j) {
-      if (kk == 0 || !cand_of(j)) continue;
+      if (!cand_of(j)) continue;
       const float sc = score_of(j);
       const uint32_t key = order_key(sc);
-      bool take = false;
-      if (key > T) take = true;
-      else if (key == T) { take = e < need; ++e; }
-      if (take) {
+      int r = -1;
+      if (key > T) {
+        r = g + min(e, need);
+        ++g;
+      } else if (key == T) {
+        if (e < need) r = g + e;
+        ++e;
+      }
+      if (r >= 0) {
         out_pos[r] = j;
         if (out_sc) out_sc[r] = sc;
-        ++r;
       }
     }
   }
