@@ -23,13 +23,14 @@
 
 namespace {
 
-// One workgroup per virtual sequence s = 2b + v.
+// One workgroup per (virtual sequence s = 2b + v, head h): head 0's writes the
+// view's table row; each copies its head's part of the first private page.
 __global__ __launch_bounds__(256) void fork_kernel(
     const int32_t* __restrict__ block_table, int maxp, int log2ps,
     const int32_t* __restrict__ cu_k, const int32_t* __restrict__ verify_start,
     int view_page_base, int pages_per_view, int32_t* __restrict__ view_table,
-    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int row_elems) {
-  const int s = blockIdx.x, b = s >> 1;
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int H) {
+  const int s = blockIdx.x, b = s >> 1, h = blockIdx.y;
   const int ps = 1 << log2ps;
   const int L = cu_k[b + 1] - cu_k[b];
   const int vs = verify_start[b];
@@ -37,21 +38,20 @@ __global__ __launch_bounds__(256) void fork_kernel(
   const int n_pages = (L + ps - 1) >> log2ps;
   const int priv0 = view_page_base + s * pages_per_view;
   const int32_t* src_row = block_table + (size_t)b * maxp;
-  int32_t* dst_row = view_table + (size_t)s * maxp;
-  for (int j = threadIdx.x; j < maxp; j += blockDim.x)
-    dst_row[j] = j < first_pg ? src_row[j] : (j < n_pages ? priv0 + (j - first_pg) : -1);
+  if (h == 0) {
+    int32_t* dst_row = view_table + (size_t)s * maxp;
+    for (int j = threadIdx.x; j < maxp; j += blockDim.x)
+      dst_row[j] = j < first_pg ? src_row[j] : (j < n_pages ? priv0 + (j - first_pg) : -1);
+  }
   // the shared positions of the first private page: first_pg * ps .. vs - 1;
   // in the [page, head, offset, dim] layout one page is H * ps rows of D
   const int keep = vs - first_pg * ps;
   if (keep <= 0 || first_pg >= n_pages) return;
   const int src_page = src_row[first_pg];
-  const int H_ps = row_elems;  // H * ps rows per page
-  const size_t page_elems = (size_t)H_ps * 128;
+  const size_t page_elems = (size_t)H * ps * 128;
   // rows (h, off) with off < keep; 16-byte chunks, 16 per 128-wide row
-  const int n_chunks = (H_ps >> log2ps) * keep * 16;
-  for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) {
-    const int ch = c & 15, r = c >> 4;
-    const int off = r % keep, h = r / keep;
+  for (int c = threadIdx.x; c < keep * 16; c += blockDim.x) {
+    const int ch = c & 15, off = c >> 4;
     const size_t e = ((size_t)h * ps + off) * 128 + ch * 8;
     *(u32x4_t*)(kc + (size_t)priv0 * page_elems + e) = *(const u32x4_t*)(kc + (size_t)src_page * page_elems + e);
     *(u32x4_t*)(vc + (size_t)priv0 * page_elems + e) = *(const u32x4_t*)(vc + (size_t)src_page * page_elems + e);
@@ -96,8 +96,8 @@ extern "C" fc_status_t fv_fork_view_pages(void* k_cache, void* v_cache, const in
                                           int32_t view_page_base, int32_t pages_per_view,
                                           int32_t* view_block_table, fc_stream_t stream) {
   fc_clear_error();
-  FC_REQUIRE(B >= 1 && n_heads >= 1 && max_pages_per_seq >= 1 && view_page_base >= 0 &&
-                 pages_per_view >= 1, FC_ERR_INVALID_VALUE,
+  FC_REQUIRE(B >= 1 && n_heads >= 1 && n_heads <= 65535 && max_pages_per_seq >= 1 &&
+                 view_page_base >= 0 && pages_per_view >= 1, FC_ERR_INVALID_VALUE,
              "fv_fork_view_pages: bad sizes B=%d n_heads=%d max_pages_per_seq=%d "
              "view_page_base=%d pages_per_view=%d", B, n_heads, max_pages_per_seq,
              view_page_base, pages_per_view);
@@ -116,10 +116,10 @@ extern "C" fc_status_t fv_fork_view_pages(void* k_cache, void* v_cache, const in
                                                (hipStream_t)stream);
     if (s != FC_OK) return s;
   }
-  hipLaunchKernelGGL(fork_kernel, dim3(2 * B), dim3(256), 0, (hipStream_t)stream, block_table,
-                     max_pages_per_seq, fc_log2i(page_size), cu_seqlens_k, verify_start,
-                     view_page_base, pages_per_view, view_block_table, (uint16_t*)k_cache,
-                     (uint16_t*)v_cache, n_heads * page_size);
+  hipLaunchKernelGGL(fork_kernel, dim3(2 * B, n_heads), dim3(256), 0, (hipStream_t)stream,
+                     block_table, max_pages_per_seq, fc_log2i(page_size), cu_seqlens_k,
+                     verify_start, view_page_base, pages_per_view, view_block_table,
+                     (uint16_t*)k_cache, (uint16_t*)v_cache, n_heads);
   return fc_check_launch("fv_fork_view_pages");
 }
 
