@@ -158,6 +158,67 @@ def test_topk_verify_linear_assemble_argument_checks():
         assert ei.value.status_name == "FC_ERR_INVALID_VALUE"
 
 
+def _rejects(status_name, fn, *args):
+    with pytest.raises(fc.FlashCacheError) as ei:
+        fn(*args, stream=0)
+    assert ei.value.status_name == status_name, str(ei.value)
+
+
+def test_verify_side_argument_checks():
+    """Host checks of the two-view, commit, LM-head and confidence entry points:
+    rejected before anything is enqueued (the pointers are never touched)."""
+    _lib()
+    F = FAKE
+    # confidence-aware acceptance
+    _rejects("FC_ERR_INVALID_VALUE", fc.fv_confidence_accept, F, 100, F, 0, 4, 0.9, 1, F, F, F)
+    _rejects("FC_ERR_INVALID_VALUE", fc.fv_confidence_accept, F, 100, F, 1, 4, 0.0, 1, F, F, F)
+    _rejects("FC_ERR_INVALID_VALUE", fc.fv_confidence_accept, None, 100, F, 1, 4, 0.9, 1, F, F, F)
+    fc.fv_confidence_accept(None, 100, F, 1, 0, 0.9, 1, None, None, None, stream=0)  # no rows
+    # fork of view-private pages
+    fork = lambda **kw: dict(dict(k_cache=F, v_cache=F, block_table=F, max_pages_per_seq=8,
+                                  page_size=16, cu_seqlens_k=F, verify_start=F, B=2, n_heads=4,
+                                  head_dim=128, view_page_base=100, pages_per_view=3,
+                                  view_block_table=F), **kw)
+    for kw, st in ((dict(B=0), "FC_ERR_INVALID_VALUE"), (dict(head_dim=64), "FC_ERR_UNSUPPORTED"),
+                   (dict(page_size=12), "FC_ERR_INVALID_VALUE"), (dict(pages_per_view=0), "FC_ERR_INVALID_VALUE"),
+                   (dict(verify_start=None), "FC_ERR_INVALID_VALUE"),
+                   (dict(view_page_base=2 ** 31 - 10), "FC_ERR_INVALID_VALUE")):
+        with pytest.raises(fc.FlashCacheError) as ei:
+            fc.fv_fork_view_pages(**fork(**kw), stream=0)
+        assert ei.value.status_name == st, (kw, str(ei.value))
+    # commit
+    commit = lambda **kw: dict(dict(k_cache=F, v_cache=F, block_table=F, view_block_table=F,
+                                    max_pages_per_seq=8, page_size=16, cu_positions=F,
+                                    verify_start=F, B=2, n_positions=10, accept_pos=F, n_heads=4,
+                                    head_dim=128), **kw)
+    for kw, st in ((dict(n_heads=0), "FC_ERR_INVALID_VALUE"), (dict(head_dim=96), "FC_ERR_UNSUPPORTED"),
+                   (dict(accept_pos=None), "FC_ERR_INVALID_VALUE"), (dict(page_size=3), "FC_ERR_INVALID_VALUE")):
+        with pytest.raises(fc.FlashCacheError) as ei:
+            fc.fv_commit_accepted(**commit(**kw), stream=0)
+        assert ei.value.status_name == st, (kw, str(ei.value))
+    fc.fv_commit_accepted(**commit(n_positions=0), stream=0)   # nothing to commit
+    # LM head: vocabulary and width the tile pipeline does not take, odd row count,
+    # small workspace
+    lm = lambda **kw: dict(dict(hidden=F, w_lm=F, d_model=512, vocab=2048, cu_positions=F, B=2,
+                                R=8, draft_tokens=F, tau=0.9, workspace=F,
+                                workspace_bytes=fc.fv_lmhead_workspace_size(8, 2048), argmax=F,
+                                conf=F, accept_row=F, accept_pos=F), **kw)
+    for kw, st in ((dict(vocab=2000), "FC_ERR_UNSUPPORTED"), (dict(d_model=500), "FC_ERR_UNSUPPORTED"),
+                   (dict(R=7), "FC_ERR_INVALID_VALUE"), (dict(tau=1.5), "FC_ERR_INVALID_VALUE"),
+                   (dict(workspace_bytes=16), "FC_ERR_WORKSPACE"), (dict(hidden=None), "FC_ERR_INVALID_VALUE")):
+        with pytest.raises(fc.FlashCacheError) as ei:
+            fc.fv_lmhead_verify_accept(**lm(**kw), stream=0)
+        assert ei.value.status_name == st, (kw, str(ei.value))
+    assert fc.fv_lmhead_workspace_size(8, 2048) == 8 * 16 * 12
+    assert fc.fv_lmhead_workspace_size(0, 2048) == 0
+    # measurement probes
+    _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_kv_stream, F, F, F, 8, 16, F, 2, 4, 128, 3, F)
+    _rejects("FC_ERR_UNSUPPORTED", fc.fc_probe_kv_stream, F, F, F, 8, 16, F, 2, 4, 64, 1, F)
+    _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_kv_stream, F, F, F, 8, 12, F, 2, 4, 128, 1, F)
+    _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_mfma_bf16, 0, 10, F)
+    _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_mfma_bf16, 4, 10, None)
+
+
 def test_last_error_message_names_the_call():
     lib = _lib()
     st = lib.fc_importance_topk(None, None, 0, 0, 0, None, 0, None, None, None, None)
