@@ -198,7 +198,7 @@ __global__ void lmhead_positions(const uint8_t* __restrict__ accept_row,
 
 extern "C" size_t fv_lmhead_workspace_size(int32_t R, int32_t vocab) {
   if (R <= 0 || vocab <= 0) return 0;
-  const size_t n_part = 2 * (size_t)((vocab + 255) / 256);
+  const size_t n_part = 2 * (((size_t)vocab + 255) / 256);
   return (size_t)R * n_part * sizeof(Part);
 }
 

@@ -142,6 +142,36 @@ int main(void) {
   expect("validate ps", fc_validate_step_inputs(I, I, I, 1, 4, 4, I, 1, 12, 8, NULL),
          FC_ERR_INVALID_VALUE);
 
+  /* verify side: confidence acceptance, views, commit, LM head, probes */
+  expect("confidence tau", fv_confidence_accept(FAKE, 100, I, 1, 4, 0.f, 1, (int32_t*)FAKE,
+                                                (float*)FAKE, (uint8_t*)FAKE, NULL),
+         FC_ERR_INVALID_VALUE);
+  expect("confidence R=0", fv_confidence_accept(NULL, 100, I, 1, 0, 0.9f, 1, NULL, NULL, NULL, NULL),
+         FC_OK);
+  expect("fork page ids", fv_fork_view_pages(FAKE, FAKE, I, 8, 16, I, I, 0x40000000, 4, 128,
+                                             0x7ffffff0, 3, (int32_t*)FAKE, NULL),
+         FC_ERR_INVALID_VALUE);
+  expect("fork head_dim", fv_fork_view_pages(FAKE, FAKE, I, 8, 16, I, I, 2, 4, 64, 100, 3,
+                                             (int32_t*)FAKE, NULL),
+         FC_ERR_UNSUPPORTED);
+  expect("commit none", fv_commit_accepted(FAKE, FAKE, I, I, 8, 16, I, I, 2, 0, NULL, 4, 128, NULL),
+         FC_OK);
+  expect("lmhead vocab", fv_lmhead_verify_accept(FAKE, FAKE, 512, 2000, I, 2, 8, I, 0.9f, FAKE, 1 << 20,
+                                                 (int32_t*)FAKE, (float*)FAKE, (uint8_t*)FAKE,
+                                                 (uint8_t*)FAKE, NULL),
+         FC_ERR_UNSUPPORTED);
+  expect("lmhead size", fv_lmhead_verify_accept(FAKE, FAKE, 0x7fffffc0, 0x7fffff00, I, 2, 8, I, 0.9f,
+                                                FAKE, 1 << 20, (int32_t*)FAKE, (float*)FAKE,
+                                                (uint8_t*)FAKE, (uint8_t*)FAKE, NULL),
+         FC_ERR_UNSUPPORTED);
+  if (fv_lmhead_workspace_size(0x7fffffff, 0x7fffffff) == 0) {
+    fprintf(stderr, "FAIL lmhead workspace size\n");
+    ++failures;
+  }
+  expect("probe passes", fc_probe_kv_stream(FAKE, FAKE, I, 8, 16, I, 2, 4, 128, 3, FAKE, NULL),
+         FC_ERR_INVALID_VALUE);
+  expect("probe mfma", fc_probe_mfma_bf16(0, 10, FAKE, NULL), FC_ERR_INVALID_VALUE);
+
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;
