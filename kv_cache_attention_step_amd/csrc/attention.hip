@@ -29,8 +29,8 @@
 //     O and reduces P over the query rows: a 5-step transpose-reduce across the
 //     32 lanes of each half-wave leaves one key sum per lane, and the four waves
 //     are summed in fixed order through LDS. No float atomics: importance is
-//     deterministic. The second K pass mostly hits L2/MALL (the same head's keys
-//     were just read).
+//     deterministic. Pass 2 walks the key tiles backwards, so it starts on the
+//     keys pass 1 read last, which are the likeliest to be still in L2/MALL.
 //   * Without importance (verify pass) a single online-softmax pass is used.
 #include "fc_common.hpp"
 
@@ -451,11 +451,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
       const float off = row_ok ? mf + __builtin_amdgcn_logf(lf) : INFINITY;
 
       // ---------------- pass 2: P, O += P V, importance ----------------
-      load_group<PS_GE16, true, POL>(a, bt, h, 0, L, wave, lane, tr);
+      // tiles in reverse order (tile n_tiles keys past L: an empty prefetch)
+      load_group<PS_GE16, true, POL>(a, bt, h, max(n_tiles - 1, 0), L, wave, lane, tr);
       store_group<true>(lds, wave, lane, tr);
       __syncthreads();
       for (int tile = 0; tile < n_tiles; ++tile) {
-        load_group<PS_GE16, true, POL>(a, bt, h, tile + 1, L, wave, lane, tr);
+        const int tt = n_tiles - 1 - tile;  // key tile consumed in this iteration
+        load_group<PS_GE16, true, POL>(a, bt, h, tt > 0 ? tt - 1 : n_tiles, L, wave, lane, tr);
         const char* ks = lds + (tile & 1) * A_STAGE;
         const char* vs = ks + K_TILE;
         float* rb = red + (tile & 1) * 4 * AKT;
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         store_group<true>(lds + ((tile + 1) & 1) * A_STAGE, wave, lane, tr);
         __syncthreads();
         if (t < AKT) {
-          const int key = tile * AKT + t;
+          const int key = tt * AKT + t;
           if (key < L) {
             const float v = KS ? rb[(t >> 5) * 2 * AKT + t] + rb[((t >> 5) * 2 + 1) * AKT + t]
                                : rb[t] + rb[AKT + t] + rb[2 * AKT + t] + rb[3 * AKT + t];
