@@ -6,9 +6,12 @@
 //   1. score_j = sum over heads (ascending head order, fp32) of importance[h, j],
 //      kept in LDS with the candidate flag (sequences longer than the LDS
 //      holds recompute them from global memory in every pass instead);
-//   2. exact radix select (4 passes of 8 bits over an order-preserving uint32
-//      image of the score, LDS histograms with integer atomics) finds the k-th
-//      largest score T and how many entries equal to T are still needed;
+//   2. exact radix select over an order-preserving uint32 image of the score
+//      finds the k-th largest score T and how many entries equal to T are still
+//      needed: the bits that the smallest and largest candidate share are known
+//      from a block min/max, so passes of 8 bits (256-bin LDS histograms with
+//      integer atomics, two barriers each) cover only the bits below that common
+//      prefix;
 //   3. entries above T, plus the lowest-position entries equal to T, are chosen;
 //      a block-wide prefix count turns the chosen flags into ascending output.
 // Integer counts only, so the result is deterministic.
@@ -27,6 +30,9 @@ FC_DEVICE uint32_t order_key(float s) {
 }
 
 constexpr int TK_WAVES = TK_THREADS / 64;
+constexpr int TK_RB = 8;                   // bits per radix digit (11 bits: slower)
+constexpr int TK_BINS = 1 << TK_RB;        // 256 histogram bins
+constexpr int TK_BPL = TK_BINS / 64;       // bins per lane of the scanning wave
 
 // Exclusive prefix over the block of one int per thread; returns the total.
 // Inclusive scan inside each wave by lane shuffles, then one scan of the 16 wave
@@ -76,7 +82,7 @@ FC_DEVICE void topk_select_seq(const float* __restrict__ imp, int T_k, int H,
                                const uint8_t* __restrict__ cand_mask, int k, int k0, int L,
                                int32_t* __restrict__ out_pos, float* __restrict__ out_sc,
                                int32_t* __restrict__ count_out, float* s_score, uint8_t* s_cand,
-                               int* s_hist, int* s_scan, int* s_ctl) {
+                               int* s_hist, int* s_scan, int* s_ctl, uint32_t* s_mm) {
   const int t = threadIdx.x;
   auto score_of = [&](int j) -> float {
     if (STREAM) return head_sum_at(imp, (size_t)k0 + j, T_k, H);
@@ -91,6 +97,7 @@ FC_DEVICE void topk_select_seq(const float* __restrict__ imp, int T_k, int H,
   //    up to 32 loads are issued before their additions (one memory latency per
   //    key for up to 32 heads)
   int my_cand = 0;
+  uint32_t kmin = STREAM ? 0u : 0xFFFFFFFFu, kmax = STREAM ? 0xFFFFFFFFu : 0u;
   for (int j = t; j < L; j += TK_THREADS) {
     if (STREAM) {
       my_cand += cand_of(j);
@@ -118,33 +125,63 @@ FC_DEVICE void topk_select_seq(const float* __restrict__ imp, int T_k, int H,
     const uint8_t c = cand_mask ? (uint8_t)(cand_mask[k0 + j] != 0) : (uint8_t)1;
     s_cand[j] = c;
     my_cand += c;
+    if (c) {
+      kmin = min(kmin, order_key(s));
+      kmax = max(kmax, order_key(s));
+    }
   }
+  // block min / max of the candidates' keys (streamed sequences: the full range);
+  // the wave results travel through LDS behind the scan's barriers, which also
+  // order the zeroing of the first histogram before its use
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if ((t & 63) == 0) {
+    s_mm[(t >> 6) * 2] = kmin;
+    s_mm[(t >> 6) * 2 + 1] = kmax;
+  }
+  for (int i = t; i < TK_BINS; i += TK_THREADS) s_hist[i] = 0;
   int excl;
   const int n_cand = block_exclusive_scan(my_cand, s_scan, &excl);
   const int kk = min(k, n_cand);
+#pragma unroll
+  for (int w = 0; w < TK_WAVES; ++w) {
+    kmin = min(kmin, s_mm[2 * w]);
+    kmax = max(kmax, s_mm[2 * w + 1]);
+  }
 
-  // 2. radix select of the kk-th largest key
-  uint32_t prefix = 0, prefix_mask = 0;
+  // 2. radix select of the kk-th largest key, below the common prefix of the
+  //    candidates' keys (cp bits; cp = 32: every candidate has the same key)
+  const int cp = kmin == kmax ? 32 : __clz((int)(kmin ^ kmax));
+  uint32_t prefix_mask = cp == 0 ? 0u : (0xFFFFFFFFu << (32 - cp));
+  uint32_t prefix = kmin & prefix_mask;
   int need = kk;  // how many still to take at or below the current prefix
   if (kk > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (t < 256) s_hist[t] = 0;
-      __syncthreads();
+    int hb = 0;  // histogram buffer of this pass; the other one is cleared meanwhile
+    for (int hi = 31 - cp; hi >= 0; hi -= TK_RB) {
+      const int shift = max(hi - (TK_RB - 1), 0);
+      const uint32_t dmask = (2u << (hi - shift)) - 1u;  // digit of hi - shift + 1 <= TK_RB bits
+      int* H = s_hist + hb * TK_BINS;
       for (int j = t; j < L; j += TK_THREADS) {
         if (!cand_of(j)) continue;
         const uint32_t key = order_key(score_of(j));
-        if ((key & prefix_mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255], 1);
+        if ((key & prefix_mask) == prefix) atomicAdd(&H[(key >> shift) & dmask], 1);
       }
+      // the other buffer was last read before the previous pass's second barrier
+      for (int i = t; i < TK_BINS; i += TK_THREADS) s_hist[(hb ^ 1) * TK_BINS + i] = 0;
       __syncthreads();
       // bins from the top: the chosen bin is the first (highest) one where the
       // count of keys in it and the bins above reaches `need`. One wave scans the
-      // 256 bins, four per lane (lane l: bins 255 - 4 l .. 252 - 4 l).
+      // bins, TK_BPL consecutive ones per lane, from the top.
       if (t < 64) {
-        int c4[4], tot = 0;
+        const int top = TK_BINS - 1 - TK_BPL * t;
+        int c[TK_BPL], tot = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          c4[u] = s_hist[255 - 4 * t - u];
-          tot += c4[u];
+        for (int u = 0; u < TK_BPL; ++u) {
+          c[u] = H[top - u];
+          tot += c[u];
         }
         int incl = tot;
 #pragma unroll
@@ -152,23 +189,25 @@ FC_DEVICE void topk_select_seq(const float* __restrict__ imp, int T_k, int H,
           const int y = __shfl_up(incl, off);
           if (t >= off) incl += y;
         }
-        int below = incl - tot;  // keys in the bins above this lane's four
+        int below = incl - tot;  // keys in the bins above this lane's
         if (below < need && incl >= need) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (below < need && below + c4[u] >= need) {
-              s_ctl[0] = 255 - 4 * t - u;
+          for (int u = 0; u < TK_BPL; ++u) {
+            if (below < need && below + c[u] >= need) {
+              s_ctl[0] = top - u;
               s_ctl[1] = need - below;
             }
-            below += c4[u];
+            below += c[u];
           }
         }
       }
+      // s_ctl is written again only after the next pass's first barrier, which
+      // every thread reaches after reading it here
       __syncthreads();
       prefix |= (uint32_t)s_ctl[0] << shift;
-      prefix_mask |= 255u << shift;
+      prefix_mask |= dmask << shift;
       need = s_ctl[1];
-      __syncthreads();
+      hb ^= 1;
     }
   }
   const uint32_t T = prefix;  // exact key of the kk-th largest; `need` entries equal to T are taken
@@ -231,9 +270,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     int32_t* __restrict__ topk_count, float* __restrict__ topk_score) {
   __shared__ float s_score[FC_TOPK_MAX_LEN];
   __shared__ uint8_t s_cand[FC_TOPK_MAX_LEN];
-  __shared__ int s_hist[256];
+  __shared__ int s_hist[2 * TK_BINS];
   __shared__ int s_scan[TK_WAVES + 1];
   __shared__ int s_ctl[4];
+  __shared__ uint32_t s_mm[2 * TK_WAVES];
 
   const int b = blockIdx.x;
   const int k0 = cu_k[b];
@@ -242,10 +282,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
   float* out_sc = topk_score ? topk_score + (size_t)b * k : nullptr;
   if (L > FC_TOPK_MAX_LEN)
     topk_select_seq<true>(imp, T_k, H, cand_mask, k, k0, L, out_pos, out_sc, topk_count + b,
-                          s_score, s_cand, s_hist, s_scan, s_ctl);
+                          s_score, s_cand, s_hist, s_scan, s_ctl, s_mm);
   else
     topk_select_seq<false>(imp, T_k, H, cand_mask, k, k0, L, out_pos, out_sc, topk_count + b,
-                           s_score, s_cand, s_hist, s_scan, s_ctl);
+                           s_score, s_cand, s_hist, s_scan, s_ctl, s_mm);
 }
 
 __global__ void assemble_kernel(const int32_t* __restrict__ topk_pos,
