@@ -248,6 +248,12 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
       }
       if (mb + 1 < G::MB) load_block(mb + 1, rot_c, scaled_c);  // next block's, while this one is stored
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's tile writes are done
+      // Wait for the next block's rotation loads here, before this block's
+      // stores. The compiler would place that wait after the stores, and as
+      // the stores are conditional it cannot count them among the operations
+      // left in flight, so its wait would also cover the stores (a write's
+      // full latency per block).
+      if (mb + 1 < G::MB) FC_WAIT_VMCNT(0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const u32x4_t v = *(const u32x4_t*)(((j & 1) ? rb1 : rb0) + j * 1024);
