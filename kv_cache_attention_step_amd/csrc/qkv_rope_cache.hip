@@ -461,6 +461,25 @@ extern "C" fc_status_t fc_rms_row_scale(const void* x, int32_t M, int32_t N, flo
 // the 128-row tiles leave room for on the CUs (one sequence of 128 rows at
 // d = 4096: 48 tiles, 4 splits; two sequences: 96 tiles, 2 splits); else 1.
 // 4 splits beat 2 and 8 at 128 rows (58 vs 69 and 69 us).
+// Rows of a 256-row-tile projection that the persistent 256-row kernel takes;
+// the rest (if any) follows as 128-row tiles. When the tiles leave the last
+// round over the CUs mostly idle, the 256-row tiles that fill whole rounds are
+// kept and the remaining rows become 128-row tiles (0.62 of a 256-row tile's
+// time each, the same weight gemm8_pick_bm uses): 4366 rows x 48 column tiles
+// on 256 CUs run as 3 rounds + 1 round of 128-row tiles instead of 4 rounds.
+static int qkv_rows_in_256_tiles(int T_q, int n_tiles_n, int ncu) {
+  const long tm = (T_q + 255) / 256;
+  const long rounds = (tm * n_tiles_n + ncu - 1) / ncu;
+  const long full_rounds = tm * n_tiles_n / ncu;
+  long keep = full_rounds * ncu / n_tiles_n;  // 256-row tiles that fit in whole rounds
+  if (keep >= tm || keep * 256 >= T_q) return T_q;
+  const long main_rounds = (keep * n_tiles_n + ncu - 1) / ncu;
+  const long tail_tiles = (T_q - keep * 256 + 127) / 128 * n_tiles_n;
+  const long tail_rounds = (tail_tiles + ncu - 1) / ncu;
+  // in hundredths of a 256-row round
+  return main_rounds * 100 + tail_rounds * 62 < rounds * 100 ? (int)(keep * 256) : T_q;
+}
+
 static int qkv_k_splits(int T_q, int d_model, bool write_cache) {
   if (!write_cache) return 1;
   const long tiles = (long)((T_q + 127) / 128) * (3 * d_model / QKV_BN);
@@ -560,16 +579,27 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
                          slots, log2ps, (uint16_t*)q_out, rope_tab, row_scale);
       return fc_check_launch("fc_qkv_rope_cache_write");
     }
-#define FC_QKV_LAUNCH(GT, PERS, GRID)                                                           \
+    // rows [r0, r0 + m) of the projection as tiles of GT (the kernels index rows from 0)
+#define FC_QKV_LAUNCH(GT, PERS, GRID, r0, m, tiles)                                             \
     hipLaunchKernelGGL((qkv_rope_cache_bf16_d128<GT, PERS>), dim3(GRID), dim3(GT::THREADS), 0,  \
-                       st, (const uint16_t*)hidden, T_q, (const uint16_t*)w_qkv, d_model,       \
-                       n_heads, (uint16_t*)k_cache, (uint16_t*)v_cache, slots, log2ps,            \
-                       (uint16_t*)q_out, rope_tab, row_scale, n_tiles_n, n_tiles)
+                       st, (const uint16_t*)hidden + (size_t)(r0) * d_model, m,                 \
+                       (const uint16_t*)w_qkv, d_model, n_heads, (uint16_t*)k_cache,            \
+                       (uint16_t*)v_cache, slots ? slots + (r0) : nullptr, log2ps,              \
+                       (uint16_t*)q_out + (size_t)(r0) * n_heads * head_dim,                    \
+                       rope_tab + (size_t)(r0) * (head_dim / 2),                                \
+                       row_scale ? row_scale + (r0) : nullptr, n_tiles_n, tiles)
     if (bm == 128) {
-      FC_QKV_LAUNCH(Gemm8<128>, false, n_tiles);
+      FC_QKV_LAUNCH(Gemm8<128>, false, n_tiles, 0, T_q, n_tiles);
     } else {
-      const int grid = n_tiles < fc_num_cus() ? n_tiles : fc_num_cus();
-      FC_QKV_LAUNCH(Gemm8<256>, true, grid);
+      const int ncu = fc_num_cus();
+      const int m_main = qkv_rows_in_256_tiles(T_q, n_tiles_n, ncu);
+      const int tiles_main = (m_main / 256) * n_tiles_n;
+      const int grid = tiles_main < ncu ? tiles_main : ncu;
+      if (tiles_main > 0) FC_QKV_LAUNCH(Gemm8<256>, true, grid, 0, m_main, tiles_main);
+      if (m_main < T_q) {
+        const int tiles_tail = (T_q - m_main + 127) / 128 * n_tiles_n;
+        FC_QKV_LAUNCH(Gemm8<128>, false, tiles_tail, m_main, T_q - m_main, tiles_tail);
+      }
     }
 #undef FC_QKV_LAUNCH
     return fc_check_launch("fc_qkv_rope_cache_write");
