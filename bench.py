@@ -284,12 +284,39 @@ def verify_component(torch, args):
     torch.cuda.synchronize()
     us = float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e3
     nbytes = R * cfg.vocab * 2.0 + R * 9.0 + n_pos * 5.0
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        cpu = _verify_oracle_rate(torch, logits, vlen, draft, cfg.tau, budget_s=3.0)
     del logits
     return {"rows": R, "vocab": cfg.vocab, "avg_us": round(us, 2),
             "rows_per_s": round(R / (us * 1e-6), 1),
             "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic_bytes": _traffic("verify:verify_rows")}
+            "traffic_bytes": _traffic("verify:verify_rows"),
+            "cpu_oracle": cpu}
+
+
+def _verify_oracle_rate(torch, logits, vlen, draft, tau, budget_s):
+    """Rows per second of the untuned oracle's accept test (argmax, confidence and
+    the two-view rule, fp64) on the leading sequences of the same logits, until
+    budget_s seconds are spent. numpy's element-wise work runs on one thread."""
+    import numpy as np
+    from oracle import flashcache_oracle as O
+    cu = np.concatenate([[0], np.cumsum(vlen)])
+    dr = draft.cpu().numpy()
+    rows, spent, b = 0, 0.0, 0
+    for b in range(len(vlen)):
+        r0, r1 = 2 * int(cu[b]), 2 * int(cu[b + 1])
+        bits = logits[r0:r1].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        O.verify_accept(bits, np.array([0, int(vlen[b])]), dr[cu[b]:cu[b + 1]], tau)
+        spent += time.perf_counter() - t0
+        rows += r1 - r0
+        if spent >= budget_s:
+            break
+    return {"value": round(rows / spent, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} logit rows ({b + 1} of {len(vlen)} sequences, both views), "
+                      f"{spent:.1f} s"}
 
 
 def verify_attention_component(torch, args):
@@ -536,7 +563,54 @@ def stack_main(args):
            "query_tokens_per_s": round(q_tokens * cfg.layers / (ms.sum() * 1e-3), 1),
            "step_ms_first_last": [round(float(ms[0]), 4), round(float(ms[-1]), 4)],
            "wall_s": round(wall, 3)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _stack_oracle_rate(cfg, budget_s=args.cpu_budget_s / 2)
     print(json.dumps(out), flush=True)
+
+
+def _stack_oracle_rate(cfg, budget_s):
+    """The untuned oracle on one layer of one denoising step with the full query
+    (step 3: 16 window + 48 tracked rows per sequence), one sequence at a time
+    (its own pages only) until budget_s seconds are spent: projection, RoPE, cache
+    write, attention, importance, top-k and the output projection with residual.
+    Extrapolated to all sequences and layers of a denoising step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import flashcache_oracle as O
+    from kv_cache_attention_step_amd import workload as W
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    H, D, ps, st = cfg.n_heads, cfg.head_dim, cfg.page_size, 3
+    prompt_len, cache_len, table, num_pages, cu_k = W.multistep_base(cfg)
+    kc, vc = W.stack_prefill(cfg, num_pages)
+    w_qkv, w_o = W.layer_weights(cfg, 0)
+    Q = W.step_query_lens(cfg, st)
+    hid = W.step_hidden(cfg, st, cfg.batch * Q)
+    cand = W.step_candidates(cfg, st, prompt_len, cu_k)
+    spent, n = 0.0, 0
+    for b in range(cfg.batch):
+        L = int(cache_len[b])
+        pages = table[b, :(L + ps - 1) // ps]
+        tracked = [np.arange(prompt_len[b], prompt_len[b] + cfg.block_len * st, dtype=np.int64)]
+        positions, cu_q = O.assemble_batch(tracked, prompt_len[b:b + 1] + cfg.block_len * st,
+                                           cfg.block_len)
+        h = hid[b * Q:(b + 1) * Q]
+        t0 = time.perf_counter()
+        r = O.flash_cache_step(h, positions, cu_q, np.array([0, L], np.int32), w_qkv, H, D,
+                               cfg.rope_base, kc[pages], vc[pages],
+                               np.arange(len(pages), dtype=np.int32)[None], ps,
+                               cand[cu_k[b]:cu_k[b + 1]], cfg.track, cfg.dtype,
+                               rms_eps=cfg.rms_eps)
+        x = O.f64_to_bf16_bits(O.round_bf16(r["out"].reshape(len(positions), -1)))
+        O.linear_residual(x, w_o, h, cfg.dtype)
+        spent += time.perf_counter() - t0
+        n += 1
+        if spent >= budget_s:
+            break
+    ms_step = spent / n * cfg.batch * cfg.layers * 1e3
+    return {"value": round(ms_step, 1), "unit": "ms/step", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0 of denoising step {st} ({Q} query rows per sequence) for {n} of "
+                      f"{cfg.batch} sequences, {spent:.1f} s; x {cfg.batch} sequences / {n} x "
+                      f"{cfg.layers} layers"}
 
 
 def calibration_copy(torch):
