@@ -593,7 +593,7 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
     } else {
       const int ncu = fc_num_cus();
       const int m_main = qkv_rows_in_256_tiles(T_q, n_tiles_n, ncu);
-      const int tiles_main = (m_main / 256) * n_tiles_n;
+      const int tiles_main = (m_main + 255) / 256 * n_tiles_n;  // m_main: T_q or a multiple of 256
       const int grid = tiles_main < ncu ? tiles_main : ncu;
       if (tiles_main > 0) FC_QKV_LAUNCH(Gemm8<256>, true, grid, 0, m_main, tiles_main);
       if (m_main < T_q) {
