@@ -316,21 +316,24 @@ def test_topk_length_capacity(torch_cuda):
         assert np.array_equal(gsc[b], osc[b].astype(np.float32)), f"seq {b} scores"
 
 
-@pytest.mark.parametrize("T", [200, 1300, 3000])
-def test_qkv_row_scale_every_projection_path(torch_cuda, T):
+@pytest.mark.parametrize("T,H", [(200, 8), (1300, 8), (3000, 8), (5378, 16)])
+def test_qkv_row_scale_every_projection_path(torch_cuda, T, H):
     """Projection of RMS-normalised inputs (the layer stack's use: a per-row scale
     from fc_rms_row_scale, folded into the rotation table for Q and K and applied
-    to V) at d = 1024 (12 column tiles of 256) on each projection path of a
-    256-CU device: T=200 (24 tiles of 128 rows: K split in 4, partial products
+    to V) on each projection path of a 256-CU device. At d = 1024 (12 column
+    tiles of 256): T=200 (24 tiles of 128 rows: K split in 4, partial products
     then the split epilogue), T=1300 (132 tiles of 128 rows: one pass, 128-row
-    tiles), T=3000 (persistent 256-row tiles); sampled rows against the
-    oracle's normalised projection, cache slots bit-exact, untouched cache rows
+    tiles), T=3000 (persistent 256-row tiles, the last one partly empty). At
+    d = 2048 (24 column tiles): T=5378 (persistent 256-row tiles for 5376 rows,
+    whole rounds over the CUs, then the last 2 rows as a launch of 128-row
+    tiles). Sampled rows (first, middle and last 16) against the oracle's
+    normalised projection, cache slots bit-exact, untouched cache rows
     unchanged."""
     torch = torch_cuda
     from kv_cache_attention_step_amd import flashcache as fc
     from kv_cache_attention_step_amd.runner import to_device, to_host
-    _say(f"case qkv row scale T={T}")
-    H, D, ps, eps, base = 8, 128, 16, 1e-5, 5e5
+    _say(f"case qkv row scale T={T} H={H}")
+    D, ps, eps, base = 128, 16, 1e-5, 5e5
     d = H * D
     rng = W.rng_for(77, T)
     hid = W.to_bf16_bits((rng.standard_normal((T, d)) * 3.0).astype(np.float32))
