@@ -33,9 +33,14 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
-# kernel of each step component, as rocprofv3 names it (substring match)
+# kernel of each step component, as rocprofv3 names it (substring match). A
+# (kernels, once) pair covers an entry point that may launch several matching
+# kernels per call (the projection: 256-row tiles, then 128-row tiles for the
+# rows past the last whole round): figures are per call, summed over the
+# matching dispatches and divided by the dispatches of `once`, a kernel the
+# entry point launches exactly once per call.
 KERNELS = {
-    "qkv_rope_cache_write": "qkv_rope_cache_bf16_d128",
+    "qkv_rope_cache_write": ("qkv_rope_cache_bf16_d128", "qkv_prepass_kernel"),
     "varlen_bidir_attention": "attn_bf16_d128<true",
     "attention_one_pass": "attn_bf16_d128<false",
     "importance_topk": "topk_kernel",
@@ -75,9 +80,17 @@ def per_dispatch(csv_dir: str, counter: str):
     return out
 
 
-def _mean_for(disp, substr):
-    vals = [v for (n, v) in disp.values() if substr in n]
-    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+def _names(spec):
+    """(substring of the component's kernels, substring of its once-per-call kernel)"""
+    return spec if isinstance(spec, tuple) else (spec, spec)
+
+
+def _mean_for(disp, spec):
+    """Mean per call of the counter over the component's dispatches, and the calls."""
+    sub, once = _names(spec)
+    vals = [v for (n, v) in disp.values() if sub in n]
+    calls = sum(1 for (n, _) in disp.values() if once in n)
+    return (sum(vals) / calls, calls) if vals and calls else (None, 0)
 
 
 def summarize(fetch_dir: str, write_dir: str):
@@ -92,9 +105,9 @@ def summarize(fetch_dir: str, write_dir: str):
     f_fetch = CALIB_COPY_KIB / max(copies)
     f_write = CALIB_FILL_KIB / max(fills)
     kernels = {}
-    for key, sub in KERNELS.items():
-        fk, nf = _mean_for(fetch, sub)
-        wk, nw = _mean_for(write, sub)
+    for key, spec in KERNELS.items():
+        fk, nf = _mean_for(fetch, spec)
+        wk, nw = _mean_for(write, spec)
         if fk is None or wk is None:
             continue
         kernels[key] = {
@@ -138,21 +151,27 @@ def mfma_summary(csv_dir: str, n_simd: int, n_xcd: int):
             c = r["Counter_Name"]
             d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
     out = {}
-    for key, sub in KERNELS.items():
+    for key, spec in KERNELS.items():
+        sub, once = _names(spec)
         ds = [d for d in disp.values() if sub in d["name"] and d.get("GRBM_GUI_ACTIVE")]
-        if not ds:
+        calls = sum(1 for d in disp.values() if once in d["name"])
+        if not ds or not calls:
             continue
-        mean = lambda f: sum(f(d) for d in ds) / len(ds)
+        # per call: work and time summed over the call's dispatches; the busy
+        # fraction and the clock weighted by each dispatch's busy clocks
+        per_call = lambda f: sum(f(d) for d in ds) / calls
         xcd_clocks = lambda d: d["GRBM_GUI_ACTIVE"] / n_xcd
+        clocks = sum(xcd_clocks(d) for d in ds)
+        ns = sum(d["ns"] for d in ds)
         out[key] = {
             "dispatches": len(ds),
-            "mfma_busy": round(mean(lambda d: d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) /
-                                    (xcd_clocks(d) * n_simd)), 4),
-            "bf16_mfma_flops": mean(lambda d: d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512),
-            "lds_insts": mean(lambda d: d.get("SQ_INSTS_LDS", 0.0)),
-            "lds_bank_conflict_cycles": mean(lambda d: d.get("SQ_LDS_BANK_CONFLICT", 0.0)),
-            "clock_ghz": round(mean(lambda d: xcd_clocks(d) / d["ns"] if d["ns"] > 0 else 0.0), 3),
-            "us": round(mean(lambda d: d["ns"] * 1e-3), 2)}
+            "mfma_busy": round(sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds) /
+                               (clocks * n_simd), 4),
+            "bf16_mfma_flops": per_call(lambda d: d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512),
+            "lds_insts": per_call(lambda d: d.get("SQ_INSTS_LDS", 0.0)),
+            "lds_bank_conflict_cycles": per_call(lambda d: d.get("SQ_LDS_BANK_CONFLICT", 0.0)),
+            "clock_ghz": round(clocks / ns if ns > 0 else 0.0, 3),
+            "us": round(ns * 1e-3 / calls, 2)}
     return out
 
 
