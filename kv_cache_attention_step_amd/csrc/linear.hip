@@ -47,10 +47,7 @@ __global__ __launch_bounds__(512, 1) void linear_residual_dma(const uint16_t* __
                                                               uint16_t* __restrict__ h, int M, int N,
                                                               int K, int n_tiles_n) {
   using G = Gemm8<BM>;
-  __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[G::NST > 2 ? G::STAGE : 1024];
-  char* const sts[3] = {st0, st1, st2};
+  GEMM8_LDS(G, sts);
   const int nt = blockIdx.x % n_tiles_n;
   const int mt = blockIdx.x / n_tiles_n;
   const int m0 = mt * BM, n0 = nt * G::BN;
@@ -62,7 +59,7 @@ __global__ __launch_bounds__(512, 1) void linear_residual_dma(const uint16_t* __
   const int wm = wave >> 1, wn = wave & 1;
   // wave-private 8 KB tile: 32 rows x 64 fp32 (rows with bit 2 set swap their
   // 128-byte halves, so the two row groups of a write phase use different banks)
-  char* tile = wave < 6 ? st1 + wave * 8192 : st0 + (wave - 6) * 8192;
+  char* tile = G::epi(sts, wave);
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll

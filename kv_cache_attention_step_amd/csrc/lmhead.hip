@@ -36,9 +36,7 @@ __global__ __launch_bounds__(Gemm8<256>::THREADS, 1) void lmhead_partials(
     const uint16_t* __restrict__ hidden, int M, const uint16_t* __restrict__ w, int d,
     int n_tiles_n, int n_tiles, int grp, Part* __restrict__ part) {
   using G = Gemm8<256>;
-  __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
-  char* const sts[3] = {st0, st1, st1};
+  GEMM8_LDS(G, sts);
   const int t = threadIdx.x, lane = t & 63, lr = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;

@@ -91,13 +91,8 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
     const float* __restrict__ row_scale, int n_tiles_n, int n_tiles) {
   constexpr int BM = G::BM;
   constexpr int D = 128;
-  // K-slice stages, kept as distinct objects (see Gemm8); the third is used by 128-row tiles only
-  __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[G::NST > 2 ? G::STAGE : 1024];
-  char* const sts[3] = {st0, st1, st2};
-  static_assert(!PERSIST || (G::NST == 2 && G::STAGE >= (G::THREADS / 64) * 32 * 256),
-                "persistent tiles keep the epilogue in the second stage");
+  GEMM8_LDS(G, sts);  // K-slice stages, kept as distinct objects (see Gemm8)
+  static_assert(!PERSIST || G::RING, "persistent tiles stage the epilogue in Gemm8::epi()");
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -174,7 +169,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
       }
     }
   };
-  int* s_slot = (int*)st0;  // one-shot tiles
+  int* s_slot = (int*)sts[0];  // one-shot tiles
 
   // Per 32-row block: RoPE or row scale in registers, bf16 values into a
   // wave-private 8 KB LDS tile (32 rows of 256 bytes; rows with bit 2 set swap
@@ -184,9 +179,9 @@ __global__ __launch_bounds__(G::THREADS, 1) void qkv_rope_cache_bf16_d128(
   // outputs are not read again by this kernel, and every workgroup writes its
   // 128 KB at about the same time, which would otherwise push the operand
   // slices out of L2 (1-1.5 % faster in A/B runs).
-  // (8 waves of a 128-row tile: the second stage holds waves 0-5, the third one waves 6 and 7)
-  constexpr bool one_stage = G::STAGE >= (G::THREADS / 64) * 32 * 256;
-  char* ep = (one_stage || wave < 6) ? st1 + wave * (32 * 256) : st2 + (wave - 6) * (32 * 256);
+  // (Gemm8::epi: no load lands there during the epilogue, even with the next
+  // tile's first slices requested)
+  char* ep = G::epi(sts, wave);
   // write side: row 8 (i / 4) + 4 h5 + i % 4, column nb * 32 + lr; the half
   // swap (bit 6 of the byte offset, set by h5) permutes the column blocks
   char* const wb0 = ep + h5 * 1024 + lr * 2 + h5 * 64;         // blocks 0, 2
@@ -293,10 +288,7 @@ __global__ __launch_bounds__(512, 1) void qkv_splitk_partial(
     const uint16_t* __restrict__ hidden, int M, const uint16_t* __restrict__ w, int d, int S,
     int n_cols, float* __restrict__ part, int n_tiles_n) {
   using G = Gemm8<128>;
-  __shared__ __attribute__((aligned(1024))) char st0[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[G::STAGE];
-  char* const sts[3] = {st0, st1, st2};
+  GEMM8_LDS(G, sts);
   const int split = blockIdx.x % S;
   const int tile = blockIdx.x / S;
   const int nt = tile % n_tiles_n, mt = tile / n_tiles_n;
