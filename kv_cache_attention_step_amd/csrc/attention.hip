@@ -13,10 +13,13 @@
 // that head is fetched from HBM once and shared by all query rows through LDS.
 // Per 64-key tile:
 //   * K tile [64 keys][128] and V tile [64 keys][128] are staged key-major in LDS
-//     (double buffered; the next tile's global loads are in flight while the
-//     current one is consumed). The V^T operand of the PV product is read with
-//     gfx950's transposing LDS read (ds_read_b64_tr_b16), so V needs no transpose
-//     on its way in.
+//     (double buffered; the next tile's loads are in flight while the current one
+//     is consumed). With pages of 16 keys or more they travel by direct-to-LDS
+//     buffer loads (no staging registers, no LDS writes by the waves; under the
+//     kernel's per-tile work this streams faster than staging through registers),
+//     smaller pages through registers. The V^T operand of the PV product is read
+//     with gfx950's transposing LDS read (ds_read_b64_tr_b16), so V needs no
+//     transpose on its way in.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the accumulator of a 32x32
 //     block gives each lane one query (lane % 32) and 16 keys, so row statistics
 //     need only one cross-half exchange, and the probabilities are already in the
@@ -41,7 +44,7 @@ namespace {
 constexpr int AD = 128;                 // head dim
 constexpr int AKT = 64;                 // keys per tile (4 groups of 16, one per wave)
 constexpr int AROWS = 128;              // query rows per workgroup pass
-constexpr int K_STRIDE = AD * 2 + 16;   // bytes per key row of the K tile
+constexpr int K_STRIDE = AD * 2;        // bytes per key row of the K tile (swizzled, below)
 constexpr int V_STRIDE = AD * 2;        // bytes per key row of the V tile
 constexpr int K_TILE = AKT * K_STRIDE;
 constexpr int V_TILE = AKT * V_STRIDE;
@@ -166,12 +169,17 @@ FC_DEVICE void load_group(const AttnArgs& a, const int32_t* __restrict__ bt, int
   }
 }
 
+// LDS tile layout (both staging paths): key-major rows of 256 bytes; 16-byte chunk c of
+// K row k sits at position c ^ (k & 15), so the 16 rows that one phase of an S
+// fragment read touches fall on distinct banks without padding.
 template <bool WANT_V>
 FC_DEVICE void store_group(char* stage, int g, int lane, const TileRegs& r) {
   char* ks = stage;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *(u32x4_t*)(ks + (g * 16 + (lane >> 4) + 4 * i) * K_STRIDE + (lane & 15) * 16) = r.k[i];
+  for (int i = 0; i < 4; ++i) {
+    const int key = g * 16 + (lane >> 4) + 4 * i;
+    *(u32x4_t*)(ks + key * K_STRIDE + (((lane & 15) ^ (key & 15)) * 16)) = r.k[i];
+  }
   if (WANT_V) {
     // key-major V rows; 16-byte chunk c of key row k sits at position c ^ 4 (k & 3)
     char* vs = stage + K_TILE;
@@ -183,13 +191,76 @@ FC_DEVICE void store_group(char* stage, int g, int lane, const TileRegs& r) {
   }
 }
 
+// Wave g's key group of tile `tile` (pages of 16 keys or more) straight into the LDS
+// stage by direct-to-LDS buffer loads: no staging registers and no LDS writes by the
+// wave, which only waits for its loads before the tile's barrier. An instruction
+// fills 1 KB of LDS in lane order (4 key rows); each lane fetches the chunk that
+// belongs at its position under the layout above. Keys past L read as 0.
+template <bool WANT_V, int POL>
+FC_DEVICE void dma_group(const AttnArgs& a, const int32_t* __restrict__ bt, int h, int tile, int L,
+                         int g, int lane, char* stage) {
+  const int key0 = tile * AKT + g * 16;
+  const int psm = (1 << a.log2ps) - 1;
+  const size_t head_stride = (size_t)(psm + 1) * AD;
+  const size_t page_stride = head_stride * a.H;
+  const int nvalid = min(16, L - key0);
+  int page = 0;
+  // the block table is read-only for the whole launch: through the constant
+  // address space this wave-uniform lookup is a scalar load
+  if (nvalid > 0) page = ((const __attribute__((address_space(4))) int32_t*)bt)[key0 >> a.log2ps];
+  const size_t base = (size_t)page * page_stride + (size_t)h * head_stride + (size_t)(key0 & psm) * AD;
+  const uint32_t bytes = nvalid > 0 ? (uint32_t)nvalid * AD * 2 : 0u;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.kc + base, bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vc + base, bytes);
+  const int p = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kl = (lane >> 4) + 4 * i;  // key within the group
+    const int kg = g * 16 + kl;          // key within the tile
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(stage + (g * 16 + 4 * i) * K_STRIDE), 16,
+                                             kl * K_STRIDE + ((p ^ (kg & 15)) << 4), 0, 0, POL);
+    if (WANT_V)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(stage + K_TILE + (g * 16 + 4 * i) * V_STRIDE),
+                                               16, kl * V_STRIDE + ((p ^ (4 * (kg & 3))) << 4), 0, 0, POL);
+  }
+}
+
+// Tile fetch and hand-over of the main kernel: direct-to-LDS with pages of 16 keys
+// or more, else through registers (one guarded load per key) written by land_group.
+// The scheduling barriers keep a tile's loads ahead of the work on the previous tile
+// and the wait for them behind it (left alone, the compiler moved both into the
+// middle of that work).
+template <bool PS_GE16, bool WANT_V, int POL>
+FC_DEVICE void fetch_group(const AttnArgs& a, const int32_t* __restrict__ bt, int h, int tile, int L,
+                           int g, int lane, char* stage, TileRegs& r) {
+  if (PS_GE16) {
+    dma_group<WANT_V, POL>(a, bt, h, tile, L, g, lane, stage);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    load_group<false, WANT_V, POL>(a, bt, h, tile, L, g, lane, r);
+  }
+}
+template <bool PS_GE16, bool WANT_V>
+FC_DEVICE void land_group(char* stage, int g, int lane, const TileRegs& r) {
+  if (PS_GE16) {
+    __builtin_amdgcn_sched_barrier(0);
+    FC_WAIT_VMCNT(0);
+  } else {
+    store_group<WANT_V>(stage, g, lane, r);
+  }
+}
+
 // ---- MFMA pieces -----------------------------------------------------------
 // S^T block kb (keys kb*32 .. +31 of the tile) for this wave's 32 queries.
 FC_DEVICE f32x16_t s_block(const char* ks, int kb, const bf16x8_t (&qf)[8], int lane) {
   f32x16_t s = {};
-  const char* row = ks + (kb * 32 + (lane & 31)) * K_STRIDE + (lane >> 5) * 16;
+  const int r = kb * 32 + (lane & 31);
+  const char* row = ks + r * K_STRIDE;
+  // chunk 2 kc + (lane >> 5) of key row r sits at position (2 kc) ^ x
+  const int x = (lane >> 5) ^ (r & 15);
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) s = mfma32x32x16(as_bf16x8(*(const u32x4_t*)(row + kc * 32)), qf[kc], s);
+  for (int kc = 0; kc < 8; ++kc)
+    s = mfma32x32x16(as_bf16x8(*(const u32x4_t*)(row + (((2 * kc) ^ x) << 4))), qf[kc], s);
   return s;
 }
 
@@ -330,8 +401,14 @@ FC_DEVICE int reduced_key(int kb, int lane) { return s_key(kb, (lane >> 1) & 15,
 // (the last tile of a sequence) takes the KS layout, so all four waves work on it.
 template <bool WITH_IMP, bool PS_GE16, bool KS, bool RTS = false, bool MIXED = false>
 __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[A_LDS];
-  float* red = (float*)(lds + 2 * A_STAGE);
+  // The two tile stages and the column-sum buffer are __shared__ objects of their
+  // own: with direct-to-LDS loads in flight into one stage, the compiler then sees
+  // that reads of the other stage do not depend on them (with one array it waits for
+  // every such load before each read). The tile loops are unrolled by two so that
+  // every access names its stage statically.
+  __shared__ __attribute__((aligned(1024))) char st0[A_STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[A_STAGE];
+  __shared__ __attribute__((aligned(16))) float red[A_RED / 4];
   // K/V loads: nontemporal where each block is read once per pass, the default
   // policy where neighbouring workgroups read the same blocks at the same time
   constexpr int POL = (WITH_IMP && !RTS) ? KV_POLICY : KV_POLICY_SHARED;
@@ -389,13 +466,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
     if (WITH_IMP) {
       // ---------------- pass 1: row max and normaliser (K only) ----------------
       float m = -INFINITY, l = 0.f;
-      load_group<PS_GE16, false, POL>(a, bt, h, 0, L, wave, lane, tr);
-      store_group<false>(lds, wave, lane, tr);
+      fetch_group<PS_GE16, false, POL>(a, bt, h, 0, L, wave, lane, st0, tr);
+      land_group<PS_GE16, false>(st0, wave, lane, tr);
       __syncthreads();
-      for (int tile = 0; tile < n_tiles; ++tile) {
+      auto p1_tile = [&](int tile, const char* ks, char* nxt) __attribute__((always_inline)) {
         const bool more = tile + 1 < n_tiles;
-        load_group<PS_GE16, false, POL>(a, bt, h, tile + 1, L, wave, lane, tr);
-        const char* ks = lds + (tile & 1) * A_STAGE;
+        fetch_group<PS_GE16, false, POL>(a, bt, h, tile + 1, L, wave, lane, nxt, tr);
         f32x16_t s0 = s_block(ks, KS ? kbw : 0, qf, lane);
         f32x16_t s1;
         if (!KS) s1 = s_block(ks, 1, qf, lane);
@@ -424,8 +500,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         }
         l = (m == -INFINITY ? 0.f : l * fexp2(m - mn)) + sum;
         m = mn;
-        store_group<false>(lds + ((tile + 1) & 1) * A_STAGE, wave, lane, tr);
+        land_group<PS_GE16, false>(nxt, wave, lane, tr);
         __syncthreads();
+      };
+      for (int tile = 0; tile < n_tiles; tile += 2) {
+        p1_tile(tile, st0, st1);
+        if (tile + 1 < n_tiles) p1_tile(tile + 1, st1, st0);
       }
       const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
       float mf = fmaxf(m, mo);
@@ -452,15 +532,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
 
       // ---------------- pass 2: P, O += P V, importance ----------------
       // tiles in reverse order (tile n_tiles keys past L: an empty prefetch)
-      load_group<PS_GE16, true, POL>(a, bt, h, max(n_tiles - 1, 0), L, wave, lane, tr);
-      store_group<true>(lds, wave, lane, tr);
+      fetch_group<PS_GE16, true, POL>(a, bt, h, max(n_tiles - 1, 0), L, wave, lane, st0, tr);
+      land_group<PS_GE16, true>(st0, wave, lane, tr);
       __syncthreads();
-      for (int tile = 0; tile < n_tiles; ++tile) {
-        const int tt = n_tiles - 1 - tile;  // key tile consumed in this iteration
-        load_group<PS_GE16, true, POL>(a, bt, h, tt > 0 ? tt - 1 : n_tiles, L, wave, lane, tr);
-        const char* ks = lds + (tile & 1) * A_STAGE;
+      // iteration it consumes key tile n_tiles - 1 - it from stage it mod 2
+      auto p2_tile = [&](int it, const char* ks, char* nxt, float* rb) __attribute__((always_inline)) {
+        const int tt = n_tiles - 1 - it;  // key tile consumed in this iteration
+        fetch_group<PS_GE16, true, POL>(a, bt, h, tt > 0 ? tt - 1 : n_tiles, L, wave, lane, nxt, tr);
         const char* vs = ks + K_TILE;
-        float* rb = red + (tile & 1) * 4 * AKT;
 #pragma unroll
         for (int kk = 0; kk < (KS ? 1 : 2); ++kk) {
           const int kb = KS ? kbw : kk;
@@ -475,7 +554,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
           const float colsum = transpose_reduce16(s, lane);
           if ((lane & 1) == 0) rb[wave * AKT + reduced_key(kb, lane)] = colsum;
         }
-        store_group<true>(lds + ((tile + 1) & 1) * A_STAGE, wave, lane, tr);
+        land_group<PS_GE16, true>(nxt, wave, lane, tr);
         __syncthreads();
         if (t < AKT) {
           const int key = tt * AKT + t;
@@ -490,9 +569,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
             }
           }
         }
+      };
+      for (int it = 0; it < n_tiles; it += 2) {
+        p2_tile(it, st0, st1, red);
+        if (it + 1 < n_tiles) p2_tile(it + 1, st1, st0, red + 4 * AKT);
       }
       if (KS) {  // O = O(key block 0) + O(key block 1), both already normalised
-        float* xo = (float*)lds;   // [2][64 floats x 64 lanes]; stages are free after the loop
+        float* xo = (float*)st0;   // [2][64 floats x 64 lanes]; stages are free after the loop
         if (kbw == 1) {
 #pragma unroll
           for (int db = 0; db < 4; ++db)
@@ -514,13 +597,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
     } else {
       // ---------------- single pass, online softmax ----------------
       float m = -INFINITY, l = 0.f;
-      load_group<PS_GE16, true, KV_POLICY_SHARED>(a, bt, h, 0, L, wave, lane, tr);
-      store_group<true>(lds, wave, lane, tr);
+      fetch_group<PS_GE16, true, KV_POLICY_SHARED>(a, bt, h, 0, L, wave, lane, st0, tr);
+      land_group<PS_GE16, true>(st0, wave, lane, tr);
       __syncthreads();
-      for (int tile = 0; tile < n_tiles; ++tile) {
+      auto op_tile = [&](int tile, const char* ks, char* nxt) __attribute__((always_inline)) {
         const bool more = tile + 1 < n_tiles;
-        load_group<PS_GE16, true, KV_POLICY_SHARED>(a, bt, h, tile + 1, L, wave, lane, tr);
-        const char* ks = lds + (tile & 1) * A_STAGE;
+        fetch_group<PS_GE16, true, KV_POLICY_SHARED>(a, bt, h, tile + 1, L, wave, lane, nxt, tr);
         const char* vs = ks + K_TILE;
         const int kb0 = kst ? kbw : 0;
         f32x16_t s0 = s_block(ks, kb0, qf, lane);
@@ -573,13 +655,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
           pv_chunk(vs, 1, 0, s1, o, lane);
           pv_chunk(vs, 1, 1, s1, o, lane);
         }
-        store_group<true>(lds + ((tile + 1) & 1) * A_STAGE, wave, lane, tr);
+        land_group<PS_GE16, true>(nxt, wave, lane, tr);
         __syncthreads();
+      };
+      for (int tile = 0; tile < n_tiles; tile += 2) {
+        op_tile(tile, st0, st1);
+        if (tile + 1 < n_tiles) op_tile(tile + 1, st1, st0);
       }
       float lt = l + __shfl_xor(l, 32);
       if (kst) {  // merge (m, l, O) with the wave of the other key block (split-max merge)
-        float* xo = (float*)lds;   // [2][64 x 64] O partials, then [2][64] (m, l)
-        float* xs = xo + 2 * 4096;
+        float* xo = (float*)st0;   // [2][64 x 64] O partials; (m, l) of [2][64] in red
+        float* xs = red;
         if (kbw == 1) {
 #pragma unroll
           for (int db = 0; db < 4; ++db)
