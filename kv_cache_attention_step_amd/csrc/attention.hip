@@ -330,6 +330,18 @@ FC_DEVICE void store_o(const AttnArgs& a, int q0, int row, int Q, int h, const f
     }
 }
 
+// Combine lane i with lane i ^ 32 (the two key halves of one query row): gfx950's
+// v_permlane32_swap of x with itself gives every lane both values, so the result
+// is the same in both lanes and takes no LDS round trip.
+FC_DEVICE float fmaxf_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+FC_DEVICE float add_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // DPP lane moves within rows of 16 lanes
 FC_DEVICE float dpp_mirror(float x) {      // lane i <- lane 15 - i
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
@@ -622,7 +634,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
+        tmax = fmaxf_halves(tmax) * c;
         // without the key split key 0 of the first tile is valid, so mn is finite; with it a key
         // block can be empty (L <= 32): then mn stays -inf and P = 0
         const float mn = fmaxf(m, tmax);
@@ -662,7 +674,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
         op_tile(tile, st0, st1);
         if (tile + 1 < n_tiles) op_tile(tile + 1, st1, st0);
       }
-      float lt = l + __shfl_xor(l, 32);
+      float lt = add_halves(l);
       if (kst) {  // merge (m, l, O) with the wave of the other key block (split-max merge)
         float* xo = (float*)st0;   // [2][64 x 64] O partials; (m, l) of [2][64] in red
         float* xs = red;

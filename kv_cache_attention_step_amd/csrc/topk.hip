@@ -19,6 +19,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace {
 
 constexpr int TK_THREADS = 1024;
@@ -34,27 +36,53 @@ constexpr int TK_RB = 8;                   // bits per radix digit (11 bits: slo
 constexpr int TK_BINS = 1 << TK_RB;        // 256 histogram bins
 constexpr int TK_BPL = TK_BINS / 64;       // bins per lane of the scanning wave
 
+// Wave-level scans and reductions by DPP lane moves (a few cycles each, where a
+// general lane shuffle is an LDS permute round trip).
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+FC_DEVICE int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele shifts 1, 2, 4, 8 inside
+// each row of 16 lanes (lanes shifted in from outside the row add 0), then lane 15
+// of rows 0 and 2 is added to rows 1 and 3, and lane 31 to rows 2 and 3.
+FC_DEVICE int wave_incl_scan(int x) {
+  x += dpp_i<0x111, 0xF, true>(x);   // row_shr:1
+  x += dpp_i<0x112, 0xF, true>(x);   // row_shr:2
+  x += dpp_i<0x114, 0xF, true>(x);   // row_shr:4
+  x += dpp_i<0x118, 0xF, true>(x);   // row_shr:8
+  x += dpp_i<0x142, 0xA, false>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_i<0x143, 0xC, false>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+// min and max over the 64 lanes (the result is wave-uniform): exchanges inside
+// quads, then between the quads and the halves of each row, then the four rows.
+FC_DEVICE void wave_min_max(uint32_t& mn, uint32_t& mx) {
+  auto step = [&](auto ctrl) __attribute__((always_inline)) {
+    mn = min(mn, (uint32_t)dpp_i<decltype(ctrl)::value, 0xF, false>((int)mn));
+    mx = max(mx, (uint32_t)dpp_i<decltype(ctrl)::value, 0xF, false>((int)mx));
+  };
+  step(std::integral_constant<int, 0xB1>{});    // quad xor 1
+  step(std::integral_constant<int, 0x4E>{});    // quad xor 2
+  step(std::integral_constant<int, 0x141>{});   // half-row mirror
+  step(std::integral_constant<int, 0x140>{});   // row mirror
+  uint32_t a = mn, b = mx;
+  mn = min(min((uint32_t)__builtin_amdgcn_readlane((int)a, 0), (uint32_t)__builtin_amdgcn_readlane((int)a, 16)),
+           min((uint32_t)__builtin_amdgcn_readlane((int)a, 32), (uint32_t)__builtin_amdgcn_readlane((int)a, 48)));
+  mx = max(max((uint32_t)__builtin_amdgcn_readlane((int)b, 0), (uint32_t)__builtin_amdgcn_readlane((int)b, 16)),
+           max((uint32_t)__builtin_amdgcn_readlane((int)b, 32), (uint32_t)__builtin_amdgcn_readlane((int)b, 48)));
+}
+
 // Exclusive prefix over the block of one int per thread; returns the total.
-// Inclusive scan inside each wave by lane shuffles, then one scan of the 16 wave
-// totals: two barriers per call. buf needs TK_WAVES + 1 ints.
+// Inclusive scan inside each wave, then one scan of the 16 wave totals by wave 0:
+// two barriers per call. buf needs TK_WAVES + 1 ints.
 FC_DEVICE int block_exclusive_scan(int v, int* buf, int* out_excl) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) buf[wave] = x;
   __syncthreads();
   if (wave == 0) {
     const int w = lane < TK_WAVES ? buf[lane] : 0;
-    int wx = w;
-#pragma unroll
-    for (int off = 1; off < TK_WAVES; off <<= 1) {
-      const int y = __shfl_up(wx, off);
-      if (lane >= off) wx += y;
-    }
+    const int wx = wave_incl_scan(w);
     if (lane < TK_WAVES) buf[lane] = wx - w;            // exclusive prefix of the waves
     if (lane == TK_WAVES - 1) buf[TK_WAVES] = wx;       // block total
   }
@@ -133,11 +161,7 @@ FC_DEVICE void topk_select_seq(const float* __restrict__ imp, int T_k, int H,
   // block min / max of the candidates' keys (streamed sequences: the full range);
   // the wave results travel through LDS behind the scan's barriers, which also
   // order the zeroing of the first histogram before its use
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-  }
+  wave_min_max(kmin, kmax);
   if ((t & 63) == 0) {
     s_mm[(t >> 6) * 2] = kmin;
     s_mm[(t >> 6) * 2 + 1] = kmax;
@@ -183,12 +207,7 @@ FC_DEVICE void topk_select_seq(const float* __restrict__ imp, int T_k, int H,
           c[u] = H[top - u];
           tot += c[u];
         }
-        int incl = tot;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_up(incl, off);
-          if (t >= off) incl += y;
-        }
+        const int incl = wave_incl_scan(tot);
         int below = incl - tot;  // keys in the bins above this lane's
         if (below < need && incl >= need) {
 #pragma unroll
