@@ -635,11 +635,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128(AttnArgs a) {
           for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s1[i]);
         }
         tmax = fmaxf_halves(tmax) * c;
-        // without the key split key 0 of the first tile is valid, so mn is finite; with it a key
-        // block can be empty (L <= 32): then mn stays -inf and P = 0
-        const float mn = fmaxf(m, tmax);
+        // The exponent reference m moves only when this tile's max exceeds it by more
+        // than 8 (log2 units), so O and l are rarely rescaled; P = exp2(s c - m) then
+        // stays below 2^8 and O / l is the same. Without the key split key 0 of the
+        // first tile is valid, so m becomes finite there; with it a key block can be
+        // empty (L <= 32): then m stays -inf and P = 0.
+        const bool bump = fmaxf(m, tmax) > m + 8.f;   // true on the first key seen
+        const float mn = bump ? tmax : m;
         const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = m == -INFINITY ? 0.f : fexp2(m - mn);  // o = 0 while m = -inf
+        const float alpha = m == -INFINITY ? 0.f : (bump ? fexp2(m - mn) : 1.f);  // o = 0 while m = -inf
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
