@@ -57,6 +57,9 @@ def parse():
                     help="instead of the benchmark line: step throughput of the C2 layer "
                          "over batch sizes 1..64 (query 64 window + 64 tracked) or over query "
                          "lengths 32..512 per sequence (B=32); one JSON line per point")
+    ap.add_argument("--probe-policies", action="store_true",
+                    help="time the KV-stream probe on the C2 cache with each cache policy of its "
+                         "K-only pass (does a cache serve the second read of K?) and exit")
     ap.add_argument("--only", choices=tuple(COMPONENTS), default=None,
                     help="run only this verify-shaped component and print its JSON object "
                          "(for per-component counter runs; not the benchmark line)")
@@ -228,6 +231,52 @@ def measured_peaks(torch, bufs, flush, stream, reps=20):
             "kv_stream_two_pass_us": round(stream_us[2], 2),
             "kv_stream_two_pass_gbs": round(1.5 * kv_bytes / (stream_us[2] * 1e-6) / 1e9, 1),
             "kv_bytes": kv_bytes}
+
+
+def probe_policies_main(args):
+    """The two-pass K/V stream of the importance path (K, then K and V) on the C2
+    cache, with each cache policy on the K-only pass (the K and V pass stays
+    nontemporal), against one pass over K and V and one over K alone. If a policy
+    let the Infinity Cache or L2 serve the second read of K, the two-pass time would
+    fall toward the one-pass time plus a fraction of the K pass."""
+    import numpy as np
+    import torch
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd import flashcache as fc
+    from kv_cache_attention_step_amd import workload as W
+    from kv_cache_attention_step_amd.runner import StepBuffers
+    torch.cuda.set_device(0)
+    inp = W.make_step_inputs(CF.C2)
+    bufs = StepBuffers(inp, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(bufs.B * bufs.H, dtype=torch.float32, device="cuda:0")
+    kv_bytes = 2.0 * inp.T_k * bufs.H * bufs.D * 2
+    cases = [("K and V once, nontemporal", 1, 0, kv_bytes)] + [
+        (f"K ({name}), then K and V (nontemporal)", 2, pol, 1.5 * kv_bytes)
+        for pol, name in enumerate(("nontemporal", "default", "sc1", "sc0"))]
+    run = lambda c: fc.fc_probe_kv_stream(bufs.k_cache, bufs.v_cache, bufs.block_table,
+                                          inp.max_pages, inp.cfg.page_size, bufs.cu_k, bufs.B,
+                                          bufs.H, bufs.D, c[1], sink, stream, k_policy=c[2])
+    for c in cases:   # warm-up, and every case launches
+        run(c)
+    torch.cuda.synchronize()
+    times = {c[0]: [] for c in cases}
+    for rep in range(args.steps):   # interleaved, Infinity Cache evicted before each run
+        for c in cases:
+            flush.fill_(rep & 255)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run(c)
+            e1.record(stream)
+            e1.synchronize()
+            times[c[0]].append(e0.elapsed_time(e1) * 1e3)
+    for name, passes, pol, nbytes in cases:
+        us = float(np.median(times[name]))
+        print(json.dumps({"probe": "kv_stream", "case": name, "k_passes": passes, "k_policy": pol,
+                          "median_us": round(us, 2), "bytes_requested": nbytes,
+                          "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "runs": args.steps}),
+              flush=True)
 
 
 def _traffic(name):
@@ -648,6 +697,8 @@ def main():
         return
     if args.sweep:
         return sweep_main(args)
+    if args.probe_policies:
+        return probe_policies_main(args)
     if args.config == "C3":
         return stack_main(args)
     import numpy as np

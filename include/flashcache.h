@@ -414,8 +414,12 @@ fc_status_t fc_validate_step_inputs(const int32_t* positions, const int32_t* cu_
  * 64-key tiles through registers into LDS, nontemporal loads) and computes
  * nothing. k_passes = 1 reads K and V once; k_passes = 2 reads K, then K and V
  * (the two passes of the importance path). The elapsed time is the floor of
- * that pattern's memory traffic on the device. head_dim must be 128. sink
- * [B * n_heads] fp32 is a dummy output (left unchanged in practice).
+ * that pattern's memory traffic on the device. k_policy is the cache policy of
+ * the K-only pass when k_passes = 2 (0 nontemporal, as the attention kernel;
+ * 1 default; 2 sc1; 3 sc0; pages of 16 keys or more for 1..3, else
+ * FC_ERR_UNSUPPORTED); with k_passes = 1 it must be 0. The K and V pass is
+ * always nontemporal. head_dim must be 128. sink [B * n_heads] fp32 is a dummy
+ * output (left unchanged in practice).
  *
  * fc_probe_mfma_bf16: n_blocks workgroups of 4 waves, each wave running
  * iters x 8 independent v_mfma_f32_32x32x16_bf16 (32768 flops each) on
@@ -425,8 +429,8 @@ fc_status_t fc_validate_step_inputs(const int32_t* positions, const int32_t* cu_
 fc_status_t fc_probe_kv_stream(const void* k_cache, const void* v_cache,
                                const int32_t* block_table, int32_t max_pages_per_seq,
                                int32_t page_size, const int32_t* cu_seqlens_k, int32_t B,
-                               int32_t n_heads, int32_t head_dim, int32_t k_passes, float* sink,
-                               fc_stream_t stream);
+                               int32_t n_heads, int32_t head_dim, int32_t k_passes,
+                               int32_t k_policy, float* sink, fc_stream_t stream);
 fc_status_t fc_probe_mfma_bf16(int32_t n_blocks, int32_t iters, float* sink, fc_stream_t stream);
 
 #ifdef __cplusplus

@@ -14,6 +14,8 @@
 // measures the sustained dense bf16 MFMA rate at the clock the device holds.
 #include "fc_common.hpp"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int PD = 128;                 // head dim
@@ -21,7 +23,11 @@ constexpr int PKT = 64;                 // keys per tile
 constexpr int PK_STRIDE = PD * 2 + 16;  // LDS bytes per K row (as the attention kernel)
 constexpr int P_STAGE = PKT * PK_STRIDE + PKT * PD * 2;
 
-template <bool TWO_PASS>
+// Cache policy operand of the buffer loads: nontemporal (the attention kernel's K/V
+// stream), default, sc1, sc0.
+constexpr int PROBE_POLICY[4] = {2, 0, 16, 1};
+
+template <bool TWO_PASS, int P1>
 __global__ __launch_bounds__(256, 2) void kv_stream_kernel(const uint16_t* __restrict__ kc,
                                                            const uint16_t* __restrict__ vc,
                                                            const int32_t* __restrict__ block_table,
@@ -42,7 +48,8 @@ __global__ __launch_bounds__(256, 2) void kv_stream_kernel(const uint16_t* __res
   // it: with pages of 16 keys or more the group lies in one page and is read
   // through a buffer range clipped at the sequence's end (keys past L read 0,
   // an empty range reads nothing); smaller pages take one guarded load per key
-  auto load = [&](const uint16_t* base, int tile, u32x4_t (&r)[4]) {
+  // pol: the cache policy operand of the page-group loads (pages of 16 keys or more)
+  auto load = [&](const uint16_t* base, int tile, u32x4_t (&r)[4], auto pol) {
     const int key0 = tile * PKT + wave * 16;
     if (ps >= 16) {
       const int nvalid = min(16, L - key0);
@@ -53,7 +60,8 @@ __global__ __launch_bounds__(256, 2) void kv_stream_kernel(const uint16_t* __res
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + off0, nvalid > 0 ? (uint32_t)nvalid * PD * 2 : 0u);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((lane >> 4) + 4 * i) * (PD * 2) + (lane & 15) * 16, 0, 2);
+        r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((lane >> 4) + 4 * i) * (PD * 2) + (lane & 15) * 16, 0,
+                                                     decltype(pol)::value);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -73,27 +81,29 @@ __global__ __launch_bounds__(256, 2) void kv_stream_kernel(const uint16_t* __res
     for (int i = 0; i < 4; ++i)
       *(u32x4_t*)(st + (wave * 16 + (lane >> 4) + 4 * i) * stride + (lane & 15) * 16) = r[i];
   };
+  using Pol1 = std::integral_constant<int, P1>;   // first (K only) pass
+  using PolNt = std::integral_constant<int, 2>;   // the K and V pass: nontemporal
   u32x4_t acc = {0, 0, 0, 0};
   u32x4_t rk[4], rv[4];
   if (TWO_PASS) {
-    load(kc, 0, rk);
+    load(kc, 0, rk, Pol1{});
     store(lds, PK_STRIDE, rk);
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
-      load(kc, t + 1, rk);
+      load(kc, t + 1, rk, Pol1{});
       acc += *(const u32x4_t*)(lds + (t & 1) * P_STAGE + lane * 16);
       store(lds + ((t + 1) & 1) * P_STAGE, PK_STRIDE, rk);
       __syncthreads();
     }
   }
-  load(kc, 0, rk);
-  load(vc, 0, rv);
+  load(kc, 0, rk, PolNt{});
+  load(vc, 0, rv, PolNt{});
   store(lds, PK_STRIDE, rk);
   store(lds + PKT * PK_STRIDE, PD * 2, rv);
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
-    load(kc, t + 1, rk);
-    load(vc, t + 1, rv);
+    load(kc, t + 1, rk, PolNt{});
+    load(vc, t + 1, rv, PolNt{});
     const char* cur = lds + (t & 1) * P_STAGE;
     acc += *(const u32x4_t*)(cur + lane * 16) + *(const u32x4_t*)(cur + PKT * PK_STRIDE + lane * 16);
     char* nxt = lds + ((t + 1) & 1) * P_STAGE;
@@ -133,25 +143,37 @@ extern "C" fc_status_t fc_probe_kv_stream(const void* k_cache, const void* v_cac
                                           const int32_t* block_table, int32_t max_pages_per_seq,
                                           int32_t page_size, const int32_t* cu_seqlens_k, int32_t B,
                                           int32_t n_heads, int32_t head_dim, int32_t k_passes,
-                                          float* sink, fc_stream_t stream) {
+                                          int32_t k_policy, float* sink, fc_stream_t stream) {
   fc_clear_error();
   FC_REQUIRE(B >= 1 && n_heads >= 1 && (k_passes == 1 || k_passes == 2), FC_ERR_INVALID_VALUE,
              "fc_probe_kv_stream: bad sizes B=%d n_heads=%d k_passes=%d", B, n_heads, k_passes);
+  FC_REQUIRE(k_policy >= 0 && k_policy <= 3 && (k_policy == 0 || k_passes == 2),
+             FC_ERR_INVALID_VALUE,
+             "fc_probe_kv_stream: k_policy=%d must be 0..3 (and 0 with k_passes=1)", k_policy);
   FC_REQUIRE(head_dim == PD, FC_ERR_UNSUPPORTED, "fc_probe_kv_stream: head_dim must be %d", PD);
   FC_REQUIRE(k_cache && v_cache && block_table && cu_seqlens_k && sink, FC_ERR_INVALID_VALUE,
              "fc_probe_kv_stream: NULL required pointer");
   FC_REQUIRE(fc_is_pow2(page_size) && page_size <= 256 && max_pages_per_seq >= 1,
              FC_ERR_INVALID_VALUE, "fc_probe_kv_stream: page_size=%d must be a power of two <= 256",
              page_size);
+  FC_REQUIRE(k_policy == 0 || page_size >= 16, FC_ERR_UNSUPPORTED,
+             "fc_probe_kv_stream: k_policy=%d needs pages of 16 keys or more", k_policy);
   const int log2ps = fc_log2i(page_size);
-  if (k_passes == 2)
-    hipLaunchKernelGGL(kv_stream_kernel<true>, dim3(B * n_heads), dim3(256), 0, (hipStream_t)stream,
-                       (const uint16_t*)k_cache, (const uint16_t*)v_cache, block_table,
-                       max_pages_per_seq, log2ps, cu_seqlens_k, n_heads, sink);
+#define FC_KV_PROBE(TWO, POL)                                                                   \
+  hipLaunchKernelGGL((kv_stream_kernel<TWO, POL>), dim3(B * n_heads), dim3(256), 0,             \
+                     (hipStream_t)stream, (const uint16_t*)k_cache, (const uint16_t*)v_cache,   \
+                     block_table, max_pages_per_seq, log2ps, cu_seqlens_k, n_heads, sink)
+  if (k_passes == 1)
+    FC_KV_PROBE(false, PROBE_POLICY[0]);
+  else if (k_policy == 0)
+    FC_KV_PROBE(true, PROBE_POLICY[0]);
+  else if (k_policy == 1)
+    FC_KV_PROBE(true, PROBE_POLICY[1]);
+  else if (k_policy == 2)
+    FC_KV_PROBE(true, PROBE_POLICY[2]);
   else
-    hipLaunchKernelGGL(kv_stream_kernel<false>, dim3(B * n_heads), dim3(256), 0, (hipStream_t)stream,
-                       (const uint16_t*)k_cache, (const uint16_t*)v_cache, block_table,
-                       max_pages_per_seq, log2ps, cu_seqlens_k, n_heads, sink);
+    FC_KV_PROBE(true, PROBE_POLICY[3]);
+#undef FC_KV_PROBE
   return fc_check_launch("fc_probe_kv_stream");
 }
 

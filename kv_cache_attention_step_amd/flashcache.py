@@ -68,7 +68,7 @@ _SIGS = {
     "fv_fork_view_pages": ([P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, P, P], I32),
     "fv_commit_accepted": ([P, P, P, P, I32, I32, P, P, I32, I32, P, I32, I32, P], I32),
     "fv_confidence_accept": ([P, I32, P, I32, I32, F32, I32, P, P, P, P], I32),
-    "fc_probe_kv_stream": ([P, P, P, I32, I32, P, I32, I32, I32, I32, P, P], I32),
+    "fc_probe_kv_stream": ([P, P, P, I32, I32, P, I32, I32, I32, I32, I32, P, P], I32),
     "fc_probe_mfma_bf16": ([I32, I32, P, P], I32),
     "fc_varlen_bidir_attention_noalloc": ([P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, F32,
                                            P, P, I32, I32, P], I32),
@@ -208,10 +208,10 @@ def fc_varlen_bidir_attention_noalloc(q, k_cache, v_cache, block_table, max_page
 
 
 def fc_probe_kv_stream(k_cache, v_cache, block_table, max_pages_per_seq, page_size, cu_seqlens_k,
-                       B, n_heads, head_dim, k_passes, sink, stream=None):
+                       B, n_heads, head_dim, k_passes, sink, stream=None, k_policy=0):
     st = load().fc_probe_kv_stream(_p(k_cache), _p(v_cache), _p(block_table), max_pages_per_seq,
                                    page_size, _p(cu_seqlens_k), B, n_heads, head_dim, k_passes,
-                                   _p(sink), _stream(stream))
+                                   k_policy, _p(sink), _stream(stream))
     _check("fc_probe_kv_stream", st)
 
 

@@ -168,7 +168,7 @@ int main(void) {
     fprintf(stderr, "FAIL lmhead workspace size\n");
     ++failures;
   }
-  expect("probe passes", fc_probe_kv_stream(FAKE, FAKE, I, 8, 16, I, 2, 4, 128, 3, FAKE, NULL),
+  expect("probe passes", fc_probe_kv_stream(FAKE, FAKE, I, 8, 16, I, 2, 4, 128, 3, 0, FAKE, NULL),
          FC_ERR_INVALID_VALUE);
   expect("probe mfma", fc_probe_mfma_bf16(0, 10, FAKE, NULL), FC_ERR_INVALID_VALUE);
 

@@ -158,9 +158,9 @@ def test_topk_verify_linear_assemble_argument_checks():
         assert ei.value.status_name == "FC_ERR_INVALID_VALUE"
 
 
-def _rejects(status_name, fn, *args):
+def _rejects(status_name, fn, *args, **kw):
     with pytest.raises(fc.FlashCacheError) as ei:
-        fn(*args, stream=0)
+        fn(*args, stream=0, **kw)
     assert ei.value.status_name == status_name, str(ei.value)
 
 
@@ -215,6 +215,13 @@ def test_verify_side_argument_checks():
     _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_kv_stream, F, F, F, 8, 16, F, 2, 4, 128, 3, F)
     _rejects("FC_ERR_UNSUPPORTED", fc.fc_probe_kv_stream, F, F, F, 8, 16, F, 2, 4, 64, 1, F)
     _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_kv_stream, F, F, F, 8, 12, F, 2, 4, 128, 1, F)
+    # cache policy of the K pass: 0..3, only with two passes, pages of 16 keys or more
+    _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_kv_stream, F, F, F, 8, 16, F, 2, 4, 128, 2, F,
+             k_policy=4)
+    _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_kv_stream, F, F, F, 8, 16, F, 2, 4, 128, 1, F,
+             k_policy=1)
+    _rejects("FC_ERR_UNSUPPORTED", fc.fc_probe_kv_stream, F, F, F, 8, 4, F, 2, 4, 128, 2, F,
+             k_policy=1)
     _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_mfma_bf16, 0, 10, F)
     _rejects("FC_ERR_INVALID_VALUE", fc.fc_probe_mfma_bf16, 4, 10, None)
 
