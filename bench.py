@@ -57,6 +57,13 @@ def parse():
                     help="instead of the benchmark line: step throughput of the C2 layer "
                          "over batch sizes 1..64 (query 64 window + 64 tracked) or over query "
                          "lengths 32..512 per sequence (B=32); one JSON line per point")
+    ap.add_argument("--ab-lib", default=None, metavar="PATH",
+                    help="A/B in one process: time one entry point (--ab-call) of the C2 step "
+                         "(C4 for verify_attention) with another build of libflashcache.so at "
+                         "PATH against this tree's build, alternating calls, Infinity Cache "
+                         "evicted before each; checks the outputs against each other and exits")
+    ap.add_argument("--ab-call", default="attention",
+                    choices=("assemble", "qkv", "attention", "topk", "step", "verify_attention"))
     ap.add_argument("--probe-policies", action="store_true",
                     help="time the KV-stream probe on the C2 cache with each cache policy of its "
                          "K-only pass (does a cache serve the second read of K?) and exit")
@@ -277,6 +284,81 @@ def probe_policies_main(args):
                           "median_us": round(us, 2), "bytes_requested": nbytes,
                           "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "runs": args.steps}),
               flush=True)
+
+
+def ab_main(args):
+    """A/B timing of one entry point between two builds of the library in one
+    process (same inputs, same device state): calls alternate A B / B A, each after
+    the Infinity Cache is evicted, HIP events around the call. The outputs of one
+    call of each build are compared (bit-identical, or the largest difference of
+    the bf16 outputs)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd import flashcache as fc
+    from kv_cache_attention_step_amd import workload as W
+    from kv_cache_attention_step_amd.runner import StepBuffers, VerifyBuffers
+
+    def open_lib(path):
+        lib = ctypes.CDLL(os.path.abspath(path))
+        for name, (argt, res) in fc._SIGS.items():
+            f = getattr(lib, name)
+            f.argtypes, f.restype = argt, res
+        return lib
+    libs = {"A (this tree)": fc.load(), "B (" + args.ab_lib + ")": open_lib(args.ab_lib)}
+    torch.cuda.set_device(0)
+    if args.ab_call == "verify_attention":
+        vb = VerifyBuffers(W.make_verify_inputs(CF.C4, with_logits=False), device="cuda:0")
+        vb.qkv()
+        fn, outs = vb.attention, lambda: {"attn_out": vb.step.attn_out}
+    else:
+        b = StepBuffers(W.make_step_inputs(CF.C2), device="cuda:0")
+        b.run()
+        fn = {"assemble": b.assemble, "qkv": b.qkv, "attention": b.attention, "topk": b.topk,
+              "step": b.run}[args.ab_call]
+        outs = lambda: {"positions": b.positions, "q_out": b.q_out, "slot_mapping": b.slot_mapping,
+                        "attn_out": b.attn_out, "importance": b.importance,
+                        "topk_pos": b.topk_pos, "topk_count": b.topk_count}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    got = {}
+    for k, lib in libs.items():
+        fc._lib = lib
+        fn()
+        torch.cuda.synchronize()
+        got[k] = {n: t.clone() for n, t in outs().items()}
+    (ka, ga), (kb, gb) = got.items()
+    diffs = {}
+    for n in ga:
+        if not torch.equal(ga[n], gb[n]):
+            a, c = ga[n], gb[n]
+            if n in ("q_out", "attn_out"):   # bf16 bits: largest difference of the values
+                diffs[n] = float((a.view(torch.bfloat16).float() - c.view(torch.bfloat16).float())
+                                 .abs().max())
+            elif a.dtype == torch.float32:
+                diffs[n] = float((a - c).abs().max())
+            else:
+                diffs[n] = "differs"
+    t0 = time.time()
+    while time.time() - t0 < args.settle_s:
+        fn()
+    torch.cuda.synchronize()
+    times = {k: [] for k in libs}
+    for r in range(args.steps):
+        for k in (list(libs) if r % 2 == 0 else list(libs)[::-1]):
+            fc._lib = libs[k]
+            flush.fill_(r & 255)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            times[k].append(e0.elapsed_time(e1) * 1e3)
+    fc._lib = libs["A (this tree)"]
+    print(json.dumps({"ab": args.ab_call, "runs": args.steps,
+                      "median_us": {k: round(float(np.median(v)), 2) for k, v in times.items()},
+                      "min_us": {k: round(float(np.min(v)), 2) for k, v in times.items()},
+                      "outputs_bit_identical": not diffs, "output_differences": diffs}), flush=True)
 
 
 def _traffic(name):
@@ -699,6 +781,8 @@ def main():
         return sweep_main(args)
     if args.probe_policies:
         return probe_policies_main(args)
+    if args.ab_lib:
+        return ab_main(args)
     if args.config == "C3":
         return stack_main(args)
     import numpy as np
