@@ -415,15 +415,37 @@ def verify_component(torch, args):
     torch.cuda.synchronize()
     us = float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e3
     nbytes = R * cfg.vocab * 2.0 + R * 9.0 + n_pos * 5.0
+    # confidence-aware acceptance (one view, no drafts, at-least-one rule) on one row
+    # per verified position, timed the same way
+    ca = torch.empty(n_pos, dtype=torch.uint8, device="cuda:0")
+    mask_rows = logits[:n_pos]
+    ts_c = []
+    for i in range(args.warmup + args.steps):
+        with torch.cuda.stream(stream):
+            flush.fill_(2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fc.fv_confidence_accept(mask_rows, cfg.vocab, cu_p, cfg.batch, n_pos, cfg.tau, 1, am, cf,
+                                ca, stream)
+        e1.record(stream)
+        if i >= args.warmup:
+            ts_c.append((e0, e1))
+    torch.cuda.synchronize()
+    us_c = float(np.mean([a.elapsed_time(b) for a, b in ts_c])) * 1e3
+    nbytes_c = n_pos * cfg.vocab * 2.0 + n_pos * 9.0
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
         cpu = _verify_oracle_rate(torch, logits, vlen, draft, cfg.tau, budget_s=3.0)
-    del logits
+    del logits, mask_rows
     return {"rows": R, "vocab": cfg.vocab, "avg_us": round(us, 2),
             "rows_per_s": round(R / (us * 1e-6), 1),
             "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic_bytes": _traffic("verify:verify_rows"),
+            "confidence_accept": {
+                "rows": n_pos, "avg_us": round(us_c, 2),
+                "achieved_gbs": round(nbytes_c / (us_c * 1e-6) / 1e9, 1),
+                "frac_hbm": round(nbytes_c / (us_c * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
             "cpu_oracle": cpu}
 
 
