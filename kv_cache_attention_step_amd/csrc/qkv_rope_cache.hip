@@ -38,7 +38,9 @@ FC_DEVICE int find_seq(const int32_t* __restrict__ cu, int B, int row) {
 
 // Pre-pass of the bf16 path, one thread per (token, rotation pair).
 // Rotation table: (cos, sin) of positions[t] * base^(-2e/D) for pair e of
-// token t, in fp64 then rounded to fp32. One entry per (token, pair); every Q
+// token t. The angle is formed and reduced to [-pi, pi] in fp64 (freq_scale =
+// -log2(base) / (D/2) comes from the host), then fp32 sincosf of the reduced
+// angle gives the fp32 entries to about an ulp. One entry per (token, pair); every Q
 // and K head of the token reuses it. Within a token, pairs e and e + half/2
 // are adjacent (entry 2 (e mod half/2) + e div half/2), so the lane that
 // rotates both loads them with one 16-byte load.
@@ -49,7 +51,7 @@ FC_DEVICE int find_seq(const int32_t* __restrict__ cu, int B, int row) {
 // once, so the projection's epilogue reads one slot per row instead of running
 // this chain of dependent loads in every column tile.
 __global__ void qkv_prepass_kernel(const int32_t* __restrict__ positions, int T, int half,
-                                   float rope_base, float2* __restrict__ table,
+                                   double freq_scale, float2* __restrict__ table,
                                    const int32_t* __restrict__ cu_q, int B,
                                    const int32_t* __restrict__ block_table, int maxp, int log2ps,
                                    int32_t* __restrict__ slots, int32_t* __restrict__ slot_mapping,
@@ -59,12 +61,14 @@ __global__ void qkv_prepass_kernel(const int32_t* __restrict__ positions, int T,
   const int t = idx / half, e = idx - t * half;
   const int q = half / 2;
   const int p = positions[t];
-  const double inv_freq = exp2(-(double)e / (double)half * log2((double)rope_base));
-  double sn, cs;
-  sincos((double)p * inv_freq, &sn, &cs);
+  const double th = (double)p * exp2((double)e * freq_scale);
+  constexpr double TWO_PI = 6.283185307179586476925286766559;
+  const double red = fma(-rint(th * (1.0 / TWO_PI)), TWO_PI, th);   // |red| <= pi
+  float sn, cs;
+  sincosf((float)red, &sn, &cs);
   // with a row scale r (q, k, v of hidden[t] * r) the table holds (r cos, r sin)
-  const double r = row_scale ? (double)row_scale[t] : 1.0;
-  table[(size_t)t * half + 2 * (e % q) + e / q] = make_float2((float)(cs * r), (float)(sn * r));
+  const float r = row_scale ? row_scale[t] : 1.f;
+  table[(size_t)t * half + 2 * (e % q) + e / q] = make_float2(cs * r, sn * r);
   if (e == 0 && block_table) {
     const int b = find_seq(cu_q, B, t);
     const int page = block_table[(size_t)b * maxp + (p >> log2ps)];
@@ -554,7 +558,8 @@ extern "C" fc_status_t fc_qkv_rope_cache_write(
     float2* rope_tab = (float2*)workspace;
     int32_t* slots = block_table ? (int32_t*)(rope_tab + n_rot) : nullptr;
     hipLaunchKernelGGL(qkv_prepass_kernel, dim3((n_rot + 255) / 256), dim3(256), 0, st, positions,
-                       T_q, head_dim / 2, rope_base, rope_tab, cu_seqlens_q, B, block_table,
+                       T_q, head_dim / 2, -log2((double)rope_base) / (double)(head_dim / 2),
+                       rope_tab, cu_seqlens_q, B, block_table,
                        max_pages_per_seq, log2ps, slots, slot_mapping, row_scale);
     const int n_tiles = n_tiles_m * n_tiles_n;
     const int n_cols = write_cache ? 3 * d_model : d_model;
