@@ -418,10 +418,29 @@ __global__ __launch_bounds__(256) void rms_row_scale_kernel(const T* __restrict_
   __shared__ float part[256 / 64];
   const T* row = x + (size_t)blockIdx.x * N;
   float s = 0.f;
-  for (int c = threadIdx.x; c < N; c += 256) {
-    float v;
-    if constexpr (sizeof(T) == 2) v = bf16_to_f32(row[c]); else v = row[c];
-    s = fmaf(v, v, s);
+  constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte load
+  if (N % VEC == 0 && ((uintptr_t)x & 15) == 0) {
+    // 16-byte loads: whole 1 KB runs per wave instead of 2- or 4-byte pieces
+    for (int c = threadIdx.x * VEC; c < N; c += 256 * VEC) {
+      const u32x4_t w = *(const u32x4_t*)(row + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(T) == 2) {
+          const float lo = bf16lo_to_f32(w[j]), hi = bf16hi_to_f32(w[j]);
+          s = fmaf(lo, lo, s);
+          s = fmaf(hi, hi, s);
+        } else {
+          const float v = __uint_as_float(w[j]);
+          s = fmaf(v, v, s);
+        }
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < N; c += 256) {
+      float v;
+      if constexpr (sizeof(T) == 2) v = bf16_to_f32(row[c]); else v = row[c];
+      s = fmaf(v, v, s);
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
