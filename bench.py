@@ -415,38 +415,61 @@ def verify_component(torch, args):
     torch.cuda.synchronize()
     us = float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e3
     nbytes = R * cfg.vocab * 2.0 + R * 9.0 + n_pos * 5.0
-    # confidence-aware acceptance (one view, no drafts, at-least-one rule) on one row
-    # per verified position, timed the same way
-    ca = torch.empty(n_pos, dtype=torch.uint8, device="cuda:0")
-    mask_rows = logits[:n_pos]
-    ts_c = []
-    for i in range(args.warmup + args.steps):
-        with torch.cuda.stream(stream):
-            flush.fill_(2)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        fc.fv_confidence_accept(mask_rows, cfg.vocab, cu_p, cfg.batch, n_pos, cfg.tau, 1, am, cf,
-                                ca, stream)
-        e1.record(stream)
-        if i >= args.warmup:
-            ts_c.append((e0, e1))
-    torch.cuda.synchronize()
-    us_c = float(np.mean([a.elapsed_time(b) for a, b in ts_c])) * 1e3
-    nbytes_c = n_pos * cfg.vocab * 2.0 + n_pos * 9.0
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
         cpu = _verify_oracle_rate(torch, logits, vlen, draft, cfg.tau, budget_s=3.0)
-    del logits, mask_rows
+    del logits
     return {"rows": R, "vocab": cfg.vocab, "avg_us": round(us, 2),
             "rows_per_s": round(R / (us * 1e-6), 1),
             "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic_bytes": _traffic("verify:verify_rows"),
-            "confidence_accept": {
-                "rows": n_pos, "avg_us": round(us_c, 2),
-                "achieved_gbs": round(nbytes_c / (us_c * 1e-6) / 1e9, 1),
-                "frac_hbm": round(nbytes_c / (us_c * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
             "cpu_oracle": cpu}
+
+
+def confidence_component(torch, args):
+    """Confidence-aware acceptance (one view, no drafts, the at-least-one rule) at the
+    verify-shaped workload: one logit row per verified position (16..128 per sequence,
+    B=32, vocab 126464), logits drawn on the device, timed with HIP events after the
+    Infinity Cache is evicted."""
+    import numpy as np
+    from kv_cache_attention_step_amd import configs as CF
+    from kv_cache_attention_step_amd import flashcache as fc
+    from kv_cache_attention_step_amd import workload as W
+    cfg = CF.C4
+    rng = W.rng_for(cfg.seed, 0)
+    W.draw_lengths(cfg, rng)
+    _, _ = W.draw_paging(cfg, np.full(cfg.batch, cfg.cache_len_fixed), rng)
+    vlen = rng.integers(cfg.verify_len[0], cfg.verify_len[1] + 1, size=cfg.batch)
+    cu_p = torch.tensor(np.concatenate([[0], np.cumsum(vlen)]), dtype=torch.int32, device="cuda:0")
+    n_pos = int(vlen.sum())
+    gen = torch.Generator(device="cuda:0").manual_seed(cfg.seed + 1)
+    logits = (torch.randn((n_pos, cfg.vocab), generator=gen, device="cuda:0") * cfg.logit_std).to(torch.bfloat16)
+    am = torch.empty(n_pos, dtype=torch.int32, device="cuda:0")
+    cf = torch.empty(n_pos, dtype=torch.float32, device="cuda:0")
+    acc = torch.empty(n_pos, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.Stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    ts = []
+    for i in range(args.warmup + args.steps):
+        with torch.cuda.stream(stream):
+            flush.fill_(2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fc.fv_confidence_accept(logits, cfg.vocab, cu_p, cfg.batch, n_pos, cfg.tau, 1, am, cf, acc,
+                                stream)
+        e1.record(stream)
+        if i >= args.warmup:
+            ts.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e3
+    nbytes = n_pos * cfg.vocab * 2.0 + n_pos * 9.0
+    del logits
+    return {"rows": n_pos, "vocab": cfg.vocab, "avg_us": round(us, 2),
+            "rows_per_s": round(n_pos / (us * 1e-6), 1),
+            "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic_bytes": _traffic("confidence:verify_rows")}
 
 
 def _verify_oracle_rate(torch, logits, vlen, draft, tau, budget_s):
@@ -781,7 +804,8 @@ def calibration_copy(torch):
     del fill
 
 
-COMPONENTS = {"verify": "verify_component", "verify_attention": "verify_attention_component",
+COMPONENTS = {"verify": "verify_component", "confidence": "confidence_component",
+              "verify_attention": "verify_attention_component",
               "views": "verify_views_component", "lmhead": "lmhead_component"}
 
 
@@ -951,6 +975,7 @@ def main():
                 "traffic": kd["traffic_bytes"], "measured_peak": mp_hbm,
                 "frac_of_measured_peak": kd.get("frac_of_measured_stream")}
     verify = None if args.no_verify else verify_component(torch, args)
+    confidence = None if args.no_verify else confidence_component(torch, args)
     verify_attn = None if args.no_verify else verify_attention_component(torch, args)
     verify_views = None if args.no_verify else verify_views_component(torch, args)
     lmhead = None if args.no_verify else lmhead_component(torch, args)
@@ -987,6 +1012,7 @@ def main():
                    "ms_per_step_with_kernel_events": round(float(np.median(seg(0, 4))) * 1e-3, 4),
                    "ms_per_step_graph_replay": graph_ms},
         "verify_accept_c4": verify,
+        "confidence_accept_c4": confidence,
         "verify_attention_c4": verify_attn,
         "verify_two_views_c4": verify_views,
         "lmhead_verify_c4": lmhead,
